@@ -1,0 +1,198 @@
+"""Benchmark of the Muon optimizer step on one MI355X.
+
+Default workload: the 800M-style dense decoder's full optimizer step --
+144 Muon matrices (24 layers x q/k/v/o [1536,1536] + MLP [1536,6144] and
+[6144,1536]; fp32 weights, fp32 gradients, bf16 momentum, bf16
+Newton-Schulz, N = 5) plus AdamW on 49 RMSNorm gains [1536] and an untied
+embedding and LM head [32000,1536].  Inputs are synthetic (seeded) and
+resident in HBM before timing starts.
+
+One JSON line is printed.  `value` is optimizer steps/s over the timed
+steps (wall clock, synchronised on both sides).  The `roofline` object is
+for the dominant kernel (the Newton-Schulz update GEMM X <- aX + PX): its
+algorithmic flops per launch divided by its mean launch time, measured with
+HIP events on the launch stream over the same timed steps.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload (one matrix per shape group, one tensor per AdamW group) and scales
+it to the whole step by the group counts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+FP32_PEAK_TFLOPS = 157.3       # fp32 matrix
+HBM_PEAK_GBS = 8000.0
+
+HYPER = dict(lr=1e-3, wd=0.1, mu=0.95, nesterov=True, rms_scale=0.2, eps=1e-7)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense800m",
+                    help="dense800m (default), llama1p5b_gqa, moe_share, large_n5, "
+                         "large_n10, fp32_128x512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="do not bracket launches with HIP events")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, muon_T, adam_T, budget_s: float = 30.0):
+    """Time the fp64 oracle on one matrix per shape group (and one tensor per
+    AdamW group), scale by the group counts; returns the baseline dict."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import muon_oracle as mo
+
+    def f64(t):
+        return t.detach().float().cpu().double().numpy()
+
+    t_total = 0.0
+    sample = []
+    idx = 0
+    spent = 0.0
+    for grp in wl.mats:
+        P, G, M = (f64(x[idx]) for x in (muon_T.params, muon_T.grads, muon_T.moms))
+        t0 = time.perf_counter()
+        mo.muon_step(P, G, M, ns_steps=wl.ns_steps, abc=mo.NS_COEFFS, **HYPER)
+        dt = time.perf_counter() - t0
+        spent += dt
+        t_total += dt * grp.count
+        sample.append(f"1 of {grp.count} [{grp.rows},{grp.cols}] ({dt:.2f} s)")
+        idx += grp.count
+        if spent > budget_s:
+            break
+    if adam_T is not None:
+        k = 0
+        for vg in wl.vecs:
+            p, g, m, v = (f64(x[k]) for x in (adam_T.params, adam_T.grads, adam_T.m, adam_T.v))
+            t0 = time.perf_counter()
+            mo.adamw_step(p, g, m, v, lr=HYPER["lr"], wd=HYPER["wd"], t=1)
+            dt = time.perf_counter() - t0
+            t_total += dt * vg.count
+            sample.append(f"1 of {vg.count} AdamW {list(vg.shape)} ({dt:.3f} s)")
+            k += vg.count
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": 1.0 / t_total, "unit": "steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": ("fp64 numpy oracle, full step extrapolated from " + "; ".join(sample)
+                       + f"; host has {len(os.sched_getaffinity(0))} usable cores")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(every box here has a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import matrix_orthogonalizing_optimizer_amd as mo_amd
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.WORKLOADS[args.workload]
+    mo_amd._lib.lib()
+
+    T = W.make_muon_tensors(wl, dev)
+    A = W.make_adamw_tensors(wl, dev) if wl.vecs else None
+    plan = mo_amd.MuonPlan(T.params, T.grads, T.moms, ns_dtype=wl.ns_dtype)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    step_no = [0]
+
+    def opt_step():
+        step_no[0] += 1
+        plan.step(ns_steps=wl.ns_steps, workspace=ws, **HYPER)
+        if A is not None:
+            mo_amd.adamw_step(A.params, A.grads, A.m, A.v, lr=HYPER["lr"], wd=HYPER["wd"],
+                              step=step_no[0])
+
+    for _ in range(args.warmup):
+        opt_step()
+    torch.cuda.synchronize()
+
+    classes = ["momentum", "norm", "gram", "poly", "update", "apply", "rms", "adamw"]
+    mo_amd.profile_reset()
+    if not args.no_profile:
+        mo_amd.profile_enable(classes)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        opt_step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mo_amd.profile_enable([])
+    prof = {c: mo_amd.profile_read(c) for c in classes}
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    steps_per_s = 1e3 / ms_per_step
+    alg_flops, dense_flops = W.workload_ns_flops(wl)
+    ns_ms = sum(prof[c][1] for c in ("gram", "poly", "update", "apply")) / args.steps
+    peak = BF16_PEAK_TFLOPS if wl.ns_dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
+    kernels = {}
+    for c in classes:
+        n, ms, work = prof[c]
+        if n:
+            unit = "TFLOP/s" if c in ("gram", "poly", "update", "apply") else "GB/s"
+            rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+            kernels[c] = {"launches": n, "mean_ms": ms / n, "rate": rate, "unit": unit}
+    upd = prof["update"]
+    roofline = None
+    if upd[0]:
+        ach = upd[2] / (upd[1] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                    "frac": ach / peak, "traffic": None,
+                    "kernel": "ns_gemm update X <- aX + PX",
+                    "flops_per_launch": upd[2] / upd[0], "mean_launch_ms": upd[1] / upd[0]}
+    ew_bytes = wl.n_elems * W.muon_elementwise_bytes_per_elem(wl) + \
+        (wl.n_vec_elems * W.ADAMW_BYTES_PER_ELEM if wl.vecs else 0)
+    line = {
+        "metric": "Muon optimizer steps/s (+ Newton-Schulz TFLOP/s, % of bf16 MFMA peak)",
+        "value": steps_per_s, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.ns_dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded; random-init weights, Gaussian gradients)",
+        "config": {"workload": wl.key, "muon_matrices": wl.n_mats,
+                   "muon_elements": wl.n_elems, "adamw_elements": wl.n_vec_elems,
+                   "ns_steps": wl.ns_steps, "grad_dtype": str(wl.grad_dtype).split(".")[-1],
+                   "mom_dtype": str(wl.mom_dtype).split(".")[-1]},
+        "matrices_per_s": wl.n_mats * steps_per_s,
+        "ns_alg_tflop_per_step": alg_flops / 1e12,
+        "ns_tflops": (alg_flops / (ns_ms * 1e-3) / 1e12) if ns_ms > 0 else None,
+        "ns_frac_peak": (alg_flops / (ns_ms * 1e-3) / 1e12 / peak) if ns_ms > 0 else None,
+        "ns_ms_per_step": ns_ms,
+        "step_tflops_wallclock": alg_flops / (ms_per_step * 1e-3) / 1e12,
+        "elementwise_alg_gb_per_step": ew_bytes / 1e9,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, T, A)
+    print(json.dumps(line), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

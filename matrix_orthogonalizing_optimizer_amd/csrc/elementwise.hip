@@ -1,0 +1,292 @@
+// HBM-bound kernels of the Muon step and of the AdamW side path (gfx950).
+//
+//  * prep:  momentum M <- mu M + G (section 2.1, Eq. 1), the Nesterov input
+//           N = mu M + G (paragraph after Eq. 1), per-tile fp32 partial sums
+//           of N^2 for the Frobenius norm (text before Eq. 2), and N written
+//           in the Newton-Schulz dtype in both layouts (row-major iterate X
+//           and its transpose) -- one pass over G and M.
+//  * norm:  per-matrix fp64 combine of the partials -> r = 1/(||N||_F + eps).
+//           X_0 = r N is never materialised: r is applied in the epilogues of
+//           the first Gram and Update products.
+//  * apply_x0: W <- W - lr (0.2 sqrt(max(A,B)) X_0 + wd W) when N = 0
+//           iterations are requested (section 2.2, Eq. 4).
+//  * rms:   per-matrix fp64 combine of squared-update partials ->
+//           sqrt(mean(X_N^2)) (section 2.3, Algorithm 1's return value).
+//  * adamw: AdamW with bias correction and decoupled decay for non-matrix
+//           parameters (section 2.2).
+// Reductions are deterministic: fixed-shape trees, no float atomics.
+#include "mo_internal.h"
+
+namespace mo {
+
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Load 4 consecutive elements [off, off + nvalid) of a fp32 or bf16 array;
+// missing ones read as 0.  `vec` = the 4 are in range and 4-aligned.
+__device__ __forceinline__ void load4(const void* base, int dt, int64_t off, int nvalid,
+                                      bool vec, float v[4]) {
+  if (dt == F32) {
+    const float* p = static_cast<const float*>(base) + off;
+    if (vec) {
+      const float4 q = *reinterpret_cast<const float4*>(p);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = j < nvalid ? p[j] : 0.0f;
+    }
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    if (vec) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf2f(q.x & 0xffffu); v[1] = bf2f(q.x >> 16);
+      v[2] = bf2f(q.y & 0xffffu); v[3] = bf2f(q.y >> 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = j < nvalid ? bf2f(p[j]) : 0.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ void store4(void* base, int dt, int64_t off, int nvalid,
+                                       bool vec, const float v[4]) {
+  if (dt == F32) {
+    float* p = static_cast<float*>(base) + off;
+    if (vec) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < nvalid) p[j] = v[j];
+    }
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(base) + off;
+    if (vec) {
+      uint2 q;
+      q.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+      q.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+      *reinterpret_cast<uint2*>(p) = q;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < nvalid) p[j] = f2bf(v[j]);
+    }
+  }
+}
+
+// Round a value to the storage dtype (what a later load would return).
+__device__ __forceinline__ float round_to(int dt, float v) {
+  return dt == F32 ? v : bf2f(f2bf(v));
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// One 64x64 tile of the padded natural domain [A_pad, B_pad] per block.
+// Thread layout: 16 threads x 4 columns across a row, 16 rows per pass.
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
+  __shared__ float tile[64][65];
+  __shared__ float red[4];
+  const int b = blockIdx.x / p.tiles_per_mat;
+  const int t = blockIdx.x - b * p.tiles_per_mat;
+  const MatDesc md = p.desc[b];
+  const int A = md.oriented ? p.n : p.m, B = md.oriented ? p.m : p.n;
+  const int A_pad = md.oriented ? p.n_pad : p.m_pad, B_pad = md.oriented ? p.m_pad : p.n_pad;
+  const int tiles_b = B_pad >> 6;
+  const int ta = t / tiles_b, tb = t - ta * tiles_b;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int esz = p.ns_dt == F32 ? 4 : 2;
+  char* xrow = static_cast<char*>(p.x_row) + b * p.x_stride * esz;
+  char* xt = static_cast<char*>(p.x_t) + b * p.x_stride * esz;
+  void* xnat = md.oriented ? xt : xrow;     // [A_pad, B_pad]
+  void* xtr = md.oriented ? xrow : xt;      // [B_pad, A_pad]
+  const bool vec_ok = (B & 3) == 0;
+  float sq = 0.0f;
+
+  const int c = tb * 64 + tx * 4;
+  const int nvalid = max(0, min(4, B - c));
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int rl = ty + pass * 16;
+    const int r = ta * 64 + rl;
+    float n4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < A && nvalid > 0) {
+      const int64_t off = static_cast<int64_t>(r) * B + c;
+      const bool vec = vec_ok && nvalid == 4;
+      float g[4], m[4];
+      load4(md.grad, p.grad_dt, off, nvalid, vec, g);
+      if (p.has_mom) {
+        load4(md.mom, p.mom_dt, off, nvalid, vec, m);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float mn = p.mu * m[j] + g[j];
+          m[j] = mn;
+          n4[j] = p.nesterov ? p.mu * mn + g[j] : mn;
+        }
+        store4(md.mom, p.mom_dt, off, nvalid, vec, m);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) n4[j] = g[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nvalid) n4[j] = 0.0f;
+        sq += n4[j] * n4[j];
+      }
+    }
+    // natural layout (padding written as zeros)
+    store4(xnat, p.ns_dt, static_cast<int64_t>(r) * B_pad + c, 4, true, n4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[rl][tx * 4 + j] = n4[j];
+  }
+  __syncthreads();
+  // transposed layout: rows of xtr are columns of the tile
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int cl = ty + pass * 16;           // tile column -> xtr row
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = tile[tx * 4 + j][cl];
+    const int64_t off = static_cast<int64_t>(tb * 64 + cl) * A_pad + ta * 64 + tx * 4;
+    store4(xtr, p.ns_dt, off, 4, true, v);
+  }
+  const float s = block_sum_256(sq, red);
+  if (threadIdx.x == 0) p.norm_part[static_cast<int64_t>(b) * p.tiles_per_mat + t] = s;
+}
+
+// One wave per matrix: fp64 sum of its partials.
+__global__ __launch_bounds__(64) void norm_kernel(NormArgs p) {
+  const int b = blockIdx.x;
+  const float* part = p.part + static_cast<int64_t>(b) * p.tiles;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < p.tiles; i += 64) s += static_cast<double>(part[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (threadIdx.x == 0) p.rscale[b] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(p.eps)));
+}
+
+// X_N = X_0 = r N.  One 64x64 tile of the true natural domain per block.
+__global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
+  __shared__ float red[4];
+  const int b = blockIdx.x / p.tiles_per_mat;
+  const int t = blockIdx.x - b * p.tiles_per_mat;
+  const MatDesc md = p.desc[b];
+  const int A = md.oriented ? p.n : p.m, B = md.oriented ? p.m : p.n;
+  const int B_pad = md.oriented ? p.m_pad : p.n_pad;
+  const int tiles_b = (B + 63) >> 6;
+  const int ta = t / tiles_b, tb = t - ta * tiles_b;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int esz = p.ns_dt == F32 ? 4 : 2;
+  // the natural-layout copy of N
+  const char* base = static_cast<const char*>(md.oriented ? p.x_t : p.x_row) + b * p.x_stride * esz;
+  const float r0 = p.rscale[b];
+  const float lrwd = p.lrwd;
+  const int c = tb * 64 + tx * 4;
+  const int nvalid = max(0, min(4, B - c));
+  const bool vec = ((B & 3) == 0) && nvalid == 4;
+  float sq = 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int r = ta * 64 + ty + pass * 16;
+    if (r >= A || nvalid == 0) continue;
+    float x[4];
+    load4(base, p.ns_dt, static_cast<int64_t>(r) * B_pad + c, 4, true, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = j < nvalid ? r0 * x[j] : 0.0f;
+      sq += x[j] * x[j];
+    }
+    const int64_t off = static_cast<int64_t>(r) * B + c;
+    if (p.out) {
+      store4(static_cast<char*>(p.out) + b * p.s_out * esz, p.ns_dt, off, nvalid, vec, x);
+    } else {
+      float w[4];
+      load4(md.param, F32, off, nvalid, vec, w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = w[j] - (lrwd * w[j] + p.step * x[j]);
+      store4(md.param, F32, off, nvalid, vec, w);
+    }
+  }
+  if (p.rms_part) {
+    const float s = block_sum_256(sq, red);
+    if (threadIdx.x == 0) p.rms_part[static_cast<int64_t>(b) * p.tiles_per_mat + t] = s;
+  }
+}
+
+__global__ __launch_bounds__(64) void rms_kernel(RmsArgs p) {
+  const int b = blockIdx.x;
+  const float* part = p.part + static_cast<int64_t>(b) * p.tiles;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < p.tiles; i += 64) s += static_cast<double>(part[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (threadIdx.x == 0) p.update_rms[p.desc[b].out_index] = static_cast<float>(sqrt(s * p.inv_count));
+}
+
+// AdamW: each block covers kAdamElemsPerBlock consecutive elements of one
+// tensor, 8 per thread as two groups of 4.
+__global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
+  int k = 0;
+  while (k + 1 < p.count && p.t[k + 1].block0 <= blockIdx.x) ++k;
+  const AdamTensor T = p.t[k];
+  const int64_t base = (static_cast<int64_t>(blockIdx.x) - T.block0) * kAdamElemsPerBlock;
+  const float ob1 = p.one_m_beta1, ob2 = p.one_m_beta2, lrwd = p.lr * p.wd;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int64_t off = base + half * 1024 + threadIdx.x * 4;
+    if (off >= T.n) continue;
+    const int nvalid = static_cast<int>(min<int64_t>(4, T.n - off));
+    const bool vec = nvalid == 4;
+    float g[4], w[4], m[4], v[4];
+    load4(T.g, p.grad_dt, off, nvalid, vec, g);
+    load4(T.p, F32, off, nvalid, vec, w);
+    load4(T.m, F32, off, nvalid, vec, m);
+    load4(T.v, F32, off, nvalid, vec, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[j] = p.beta1 * m[j] + ob1 * g[j];
+      v[j] = p.beta2 * v[j] + ob2 * g[j] * g[j];
+      const float upd = (m[j] * p.bc1) / (sqrtf(v[j]) * p.bc2_rsqrt + p.eps);
+      w[j] = w[j] - (p.lr * upd + lrwd * w[j]);
+    }
+    store4(T.p, F32, off, nvalid, vec, w);
+    store4(T.m, F32, off, nvalid, vec, m);
+    store4(T.v, F32, off, nvalid, vec, v);
+  }
+}
+
+hipError_t launch_prep(const PrepArgs& a, int chunk, hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_norm(const NormArgs& a, int chunk, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(chunk), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_apply_x0(const ApplyX0Args& a, int chunk, hipStream_t s) {
+  hipLaunchKernelGGL(apply_x0_kernel, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_rms(const RmsArgs& a, int chunk, hipStream_t s) {
+  hipLaunchKernelGGL(rms_kernel, dim3(chunk), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL(adamw_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mo

@@ -1,0 +1,130 @@
+// Internal declarations shared by the library's translation units.
+// Device code targets gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mo {
+
+// Element type tags used for template dispatch.
+enum Dt : int { F32 = 0, BF16 = 1 };
+
+// One Muon matrix as the kernels see it.  `oriented` = 1 when rows > cols:
+// the Newton-Schulz iterate is then the transpose of the parameter.
+struct MatDesc {
+  float* param;          // fp32 [rows, cols]
+  const void* grad;      // [rows, cols]
+  void* mom;             // [rows, cols]
+  int32_t oriented;
+  int32_t out_index;     // position in the caller's list (update RMS slot)
+};
+static_assert(sizeof(MatDesc) == 32, "descriptor layout");
+
+// Momentum / X_0 preparation over one shape group (a "bin") chunk.
+// Tiles of 64x64 cover the padded natural domain [A_pad, B_pad] of every
+// matrix; each tile writes the Newton-Schulz input in both layouts.
+struct PrepArgs {
+  const MatDesc* desc;   // chunk's descriptors (chunk-local index)
+  void* x_row;           // [chunk][m_pad][n_pad]  (ns dtype)
+  void* x_t;             // [chunk][n_pad][m_pad]
+  int64_t x_stride;      // m_pad * n_pad
+  int m, n, m_pad, n_pad;
+  int tiles_per_mat;     // (m_pad / 64) * (n_pad / 64)
+  float mu;
+  int nesterov;
+  int has_mom;           // 0: N = grad (Newton-Schulz only)
+  int grad_dt, mom_dt, ns_dt;
+  float* norm_part;      // [chunk][tiles_per_mat]
+};
+
+// Per-matrix finalisation of the squared-norm partials: r = 1/(sqrt(s)+eps).
+struct NormArgs {
+  const float* part;     // [chunk][tiles]
+  int tiles;
+  float eps;
+  float* rscale;         // [chunk]
+};
+
+// Epilogue kinds of the Newton-Schulz GEMM C = A * B^T.
+enum Epi : int {
+  EPI_GRAM = 0,     // C = s^2 acc, lower tiles mirrored
+  EPI_POLY = 1,     // C = c acc + b D, lower tiles mirrored
+  EPI_UPDATE = 2,   // C = s (acc + a D), also stored transposed in Ct
+  EPI_APPLY = 3,    // x = s (acc + a D); W -= lrwd W + step x (natural layout)
+  EPI_STORE = 4     // x = s (acc + a D); out = x (natural layout, ns dtype)
+};
+
+struct GemmArgs {
+  const void* A;  int64_t sA; int lda;   // [M, K] per batch entry
+  const void* B;  int64_t sB; int ldb;   // [N, K]
+  const void* D;  int64_t sD; int ldd;   // [M, N] epilogue operand
+  void* C;        int64_t sC; int ldc;   // [M, N] output
+  void* Ct;       int64_t sCt; int ldct; // [N, M] transposed output
+  int M, N, K;                           // padded sizes (tile multiples)
+  int tiles_m, tiles_n, tiles_per_mat, batch;
+  const float* rscale;                   // per batch entry, or null (s = 1)
+  float alpha, beta;                     // out = s (alpha acc + beta D)
+  // EPI_APPLY / EPI_STORE
+  const MatDesc* desc;                   // per batch entry
+  void* out;  int64_t s_out;             // EPI_STORE output base, stride
+  int m_true, n_true;
+  float lrwd, step;                      // W <- W - (lrwd W + step x)
+  float* rms_part;                       // [batch][tiles_per_mat] or null
+};
+
+// Elementwise apply for ns_steps = 0 (X_N = X_0), and for EPI_STORE with 0
+// steps in the Newton-Schulz-only entry point.
+struct ApplyX0Args {
+  const MatDesc* desc;
+  const void* x_row;                     // [chunk][m_pad][n_pad]
+  const void* x_t;                       // [chunk][n_pad][m_pad]
+  int64_t x_stride;                      // m_pad * n_pad
+  int m, n, m_pad, n_pad;
+  int tiles_per_mat;                     // 64x64 tiles of the true domain
+  const float* rscale;
+  float lrwd, step;
+  int ns_dt;
+  void* out; int64_t s_out;              // store mode when non-null
+  float* rms_part;                       // [chunk][tiles_per_mat] or null
+};
+
+struct RmsArgs {
+  const MatDesc* desc;
+  const float* part;
+  int tiles;
+  double inv_count;      // 1 / (rows * cols)
+  float* update_rms;     // indexed by desc[i].out_index
+};
+
+constexpr int kAdamMaxTensors = 32;
+struct AdamTensor {
+  float* p; const void* g; float* m; float* v;
+  int64_t n; int64_t block0;
+};
+struct AdamArgs {
+  AdamTensor t[kAdamMaxTensors];
+  int count;
+  int grad_dt;
+  float lr, wd, beta1, beta2, eps;
+  float one_m_beta1;     // 1 - beta1 and 1 - beta2, formed on the host in
+  float one_m_beta2;     // double (1 - 0.999f in fp32 loses 1e-5 relative)
+  float bc1;             // 1 / (1 - beta1^t)
+  float bc2_rsqrt;       // 1 / sqrt(1 - beta2^t)
+};
+constexpr int kAdamElemsPerBlock = 2048;   // 256 threads x 8
+
+// Tile configurations of the GEMM (square tiles).
+enum TileCfg : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
+int tile_size(TileCfg t);
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_prep(const PrepArgs& a, int chunk, hipStream_t s);
+hipError_t launch_norm(const NormArgs& a, int chunk, hipStream_t s);
+hipError_t launch_gemm(int ns_dt, TileCfg cfg, Epi epi, const GemmArgs& a,
+                       hipStream_t s);
+hipError_t launch_apply_x0(const ApplyX0Args& a, int chunk, hipStream_t s);
+hipError_t launch_rms(const RmsArgs& a, int chunk, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s);
+
+}  // namespace mo

@@ -1,0 +1,806 @@
+// C ABI of the Muon optimizer step (declared in include/muon.h).
+//
+// Host side: argument validation (all-or-nothing), grouping of matrices by
+// oriented shape, tile choice, workspace layout, the descriptor table, and
+// the launch sequence of one step:
+//   per shape group ("bin"), per chunk of matrices that fits the workspace:
+//     prep (momentum, Nesterov input, norm partials, X_0 in both layouts)
+//     norm (r = 1 / (||N||_F + eps))
+//     N x { Gram, Poly, Update }   -- the last Update applies the step
+//     rms (optional update RMS)
+// The method is that of "Muon is Scalable for LLM Training" (section 2.1,
+// Eq. 1 and 2; section 2.2, Eq. 4; section 2.3, Algorithm 1's RMS).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "mo_internal.h"
+
+namespace {
+
+using namespace mo;
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("MO_DEBUG_SYNC");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+int64_t ru(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool finite(float x) { return std::isfinite(x); }
+
+// ------------------------------------------------------------------ profiling
+struct ProfEntry {
+  hipEvent_t start, stop;
+  double work;
+};
+struct ProfClass {
+  int64_t launches = 0;
+  double ms = 0.0, work = 0.0;
+  std::vector<ProfEntry> pending;
+};
+std::mutex g_prof_mu;
+unsigned g_prof_mask = 0;
+ProfClass g_prof[MO_K_COUNT];
+
+struct ProfScope {
+  int cls = -1;
+  hipEvent_t start = nullptr, stop = nullptr;
+  hipStream_t s = nullptr;
+  double work = 0;
+  ProfScope(int c, hipStream_t st, double w) {
+    if (!(g_prof_mask & (1u << c))) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) return;
+    cls = c;
+    s = st;
+    work = w;
+    (void)hipEventRecord(start, s);
+  }
+  ~ProfScope() {
+    if (cls < 0) return;
+    (void)hipEventRecord(stop, s);
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof[cls].pending.push_back({start, stop, work});
+  }
+};
+
+// Launch bookkeeping: checks the launch status and optionally syncs.
+int checked(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess) return fail(MO_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  if (debug_sync()) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(MO_EHIP, "%s failed: %s", what, hipGetErrorString(e));
+  }
+  return MO_OK;
+}
+
+// ------------------------------------------------------------------ planning
+struct Bin {
+  int m, n, m_pad, n_pad;
+  TileCfg cfg;
+  int first, count;        // range in the plan's descriptor order
+};
+
+struct HostPlan {
+  int grad_dt = BF16, mom_dt = BF16, ns_dt = BF16;
+  int64_t count = 0;
+  std::vector<MatDesc> descs;   // grouped by bin
+  std::vector<Bin> bins;
+  int esz() const { return ns_dt == F32 ? 4 : 2; }
+};
+
+int dt_size(int dt) { return dt == F32 ? 4 : 2; }
+
+// Tile choice for a shape group: estimated time of the padded work, scaled
+// by a per-tile efficiency and by how well the update GEMM fills 256 CUs.
+TileCfg choose_tile(int m, int n, int count, int ns_dt) {
+  if (const char* e = std::getenv("MO_TILE")) {
+    const int t = std::atoi(e);
+    if (t == 256 && ns_dt == BF16) return TILE_256;
+    if (t == 128) return TILE_128;
+    if (t == 64) return TILE_64;
+  }
+  const TileCfg cands_bf[] = {TILE_256, TILE_128, TILE_64};
+  const TileCfg cands_f[] = {TILE_128, TILE_64};
+  const TileCfg* c = ns_dt == BF16 ? cands_bf : cands_f;
+  const int nc = ns_dt == BF16 ? 3 : 2;
+  double best = 1e300;
+  TileCfg pick = c[nc - 1];
+  for (int i = 0; i < nc; ++i) {
+    const int T = tile_size(c[i]);
+    const double eff = T == 256 ? 1.0 : (T == 128 ? 0.7 : 0.35);
+    const double mp = static_cast<double>(ru(m, T)), np = static_cast<double>(ru(n, T));
+    const double work = 3.0 * mp * mp * np + mp * mp * mp;
+    const double tiles = static_cast<double>(count) * (mp / T) * (np / T);
+    const double waves = std::ceil(tiles / 256.0);
+    const double fill = tiles / (waves * 256.0);
+    const double cost = work * count / (eff * fill);
+    if (cost < best * 0.999) {
+      best = cost;
+      pick = c[i];
+    }
+  }
+  return pick;
+}
+
+int validate_dtype(int dt, const char* what) {
+  if (dt != MO_F32 && dt != MO_BF16) return fail(MO_EINVAL, "%s must be MO_F32 or MO_BF16 (got %d)", what, dt);
+  return MO_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+  int64_t idx;
+  const char* what;
+};
+
+int check_overlap(std::vector<Range>& r) {
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i)
+    if (r[i].lo < r[i - 1].hi)
+      return fail(MO_EINVAL, "tensor %lld %s overlaps tensor %lld %s", static_cast<long long>(r[i].idx),
+                  r[i].what, static_cast<long long>(r[i - 1].idx), r[i - 1].what);
+  return MO_OK;
+}
+
+constexpr int64_t kMaxDim = 1 << 24;
+constexpr int64_t kMaxPadded = (int64_t{1} << 31) - 1;
+
+int build_plan(const mo_tensor* t, int64_t count, int grad_dt, int mom_dt, int ns_dt, bool check_ptrs,
+               HostPlan& plan) {
+  int rc;
+  if ((rc = validate_dtype(grad_dt, "grad_dtype")) || (rc = validate_dtype(mom_dt, "mom_dtype")) ||
+      (rc = validate_dtype(ns_dt, "ns_dtype")))
+    return rc;
+  if (count < 0) return fail(MO_EINVAL, "count must be >= 0");
+  if (count > 0 && !t) return fail(MO_EINVAL, "tensors is NULL");
+  if (count > (int64_t{1} << 30)) return fail(MO_EINVAL, "too many tensors");
+  plan = HostPlan{};
+  plan.grad_dt = grad_dt;
+  plan.mom_dt = mom_dt;
+  plan.ns_dt = ns_dt;
+  plan.count = count;
+  std::vector<Range> ranges;
+  struct Item {
+    int m, n;
+    int64_t idx;
+  };
+  std::vector<Item> items;
+  items.reserve(count);
+  for (int64_t i = 0; i < count; ++i) {
+    const mo_tensor& x = t[i];
+    if (x.rows < 1 || x.cols < 1 || x.rows > kMaxDim || x.cols > kMaxDim)
+      return fail(MO_EINVAL, "tensor %lld: rows and cols must be in [1, 2^24]", static_cast<long long>(i));
+    const int m = static_cast<int>(std::min(x.rows, x.cols)), n = static_cast<int>(std::max(x.rows, x.cols));
+    if (ru(m, 256) * ru(n, 256) > kMaxPadded)
+      return fail(MO_EINVAL, "tensor %lld: %lld x %lld exceeds 2^31 padded elements", static_cast<long long>(i),
+                  static_cast<long long>(x.rows), static_cast<long long>(x.cols));
+    if (check_ptrs) {
+      if (!x.param || !x.grad || !x.state0)
+        return fail(MO_EINVAL, "tensor %lld: param, grad and state0 must be non-NULL", static_cast<long long>(i));
+      if (x.state1) return fail(MO_EINVAL, "tensor %lld: state1 must be NULL for Muon", static_cast<long long>(i));
+      if (!aligned16(x.param) || !aligned16(x.grad) || !aligned16(x.state0))
+        return fail(MO_EINVAL, "tensor %lld: pointers must be 16-byte aligned", static_cast<long long>(i));
+      const uintptr_t ne = static_cast<uintptr_t>(x.rows * x.cols);
+      ranges.push_back({reinterpret_cast<uintptr_t>(x.param), reinterpret_cast<uintptr_t>(x.param) + ne * 4, i, "param"});
+      ranges.push_back({reinterpret_cast<uintptr_t>(x.grad),
+                        reinterpret_cast<uintptr_t>(x.grad) + ne * dt_size(grad_dt), i, "grad"});
+      ranges.push_back({reinterpret_cast<uintptr_t>(x.state0),
+                        reinterpret_cast<uintptr_t>(x.state0) + ne * dt_size(mom_dt), i, "momentum"});
+    }
+    items.push_back({m, n, i});
+  }
+  if (check_ptrs && (rc = check_overlap(ranges))) return rc;
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+    return a.m != b.m ? a.m > b.m : a.n > b.n;
+  });
+  for (size_t i = 0; i < items.size();) {
+    size_t j = i;
+    while (j < items.size() && items[j].m == items[i].m && items[j].n == items[i].n) ++j;
+    Bin b{};
+    b.m = items[i].m;
+    b.n = items[i].n;
+    b.count = static_cast<int>(j - i);
+    b.first = static_cast<int>(plan.descs.size());
+    b.cfg = choose_tile(b.m, b.n, b.count, ns_dt);
+    const int T = tile_size(b.cfg);
+    b.m_pad = static_cast<int>(ru(b.m, T));
+    b.n_pad = static_cast<int>(ru(b.n, T));
+    for (size_t k = i; k < j; ++k) {
+      const mo_tensor& x = t[items[k].idx];
+      MatDesc d{};
+      d.param = static_cast<float*>(x.param);
+      d.grad = x.grad;
+      d.mom = x.state0;
+      d.oriented = x.rows > x.cols ? 1 : 0;
+      d.out_index = static_cast<int32_t>(items[k].idx);
+      plan.descs.push_back(d);
+    }
+    plan.bins.push_back(b);
+    i = j;
+  }
+  return MO_OK;
+}
+
+// Workspace layout ---------------------------------------------------------
+// [descriptor table (one-shot calls only)] [rscale: count floats]
+// then, reused by every bin in turn, for a chunk of `cap` matrices:
+// [norm partials] [rms partials] [X row][X^T][X' row][X'^T][S][P]
+struct BinLayout {
+  int64_t x_elems, s_elems;
+  int prep_tiles, upd_tiles, x0_tiles, rms_tiles;
+  size_t per_mat;          // bytes per matrix in the chunk region
+};
+
+BinLayout bin_layout(const Bin& b, int esz) {
+  BinLayout L{};
+  const int T = tile_size(b.cfg);
+  L.x_elems = static_cast<int64_t>(b.m_pad) * b.n_pad;
+  L.s_elems = static_cast<int64_t>(b.m_pad) * b.m_pad;
+  L.prep_tiles = (b.m_pad / 64) * (b.n_pad / 64);
+  L.upd_tiles = (b.m_pad / T) * (b.n_pad / T);
+  L.x0_tiles = static_cast<int>(((b.m + 63) / 64) * static_cast<int64_t>((b.n + 63) / 64));
+  L.rms_tiles = std::max(L.upd_tiles, L.x0_tiles);
+  L.per_mat = static_cast<size_t>(L.prep_tiles) * 4 + static_cast<size_t>(L.rms_tiles) * 4 +
+              static_cast<size_t>(4 * L.x_elems + 2 * L.s_elems) * esz;
+  return L;
+}
+
+size_t fixed_bytes(const HostPlan& p, bool with_table) {
+  size_t f = 0;
+  if (with_table) f += align_up(p.descs.size() * sizeof(MatDesc));
+  f += align_up(static_cast<size_t>(p.count) * 4);
+  return f + 8 * kAlign;   // alignment slack of the chunk regions
+}
+
+void ws_sizes(const HostPlan& p, bool with_table, size_t* full, size_t* mn) {
+  size_t mx_full = 0, mx_min = 0;
+  for (const Bin& b : p.bins) {
+    const BinLayout L = bin_layout(b, p.esz());
+    mx_full = std::max(mx_full, L.per_mat * b.count);
+    mx_min = std::max(mx_min, L.per_mat);
+  }
+  const size_t f = fixed_bytes(p, with_table);
+  if (full) *full = f + mx_full;
+  if (mn) *mn = f + mx_min;
+}
+
+struct Hyper {
+  float lr, wd, mu, a, b, c, rms_scale, eps;
+  int nesterov, ns_steps;
+  bool has_mom;
+};
+
+int validate_hyper(const Hyper& h) {
+  if (!finite(h.lr) || !finite(h.wd) || !finite(h.mu) || !finite(h.rms_scale))
+    return fail(MO_EINVAL, "lr, wd, mu and rms_scale must be finite");
+  if (!finite(h.eps) || h.eps < 0.0f) return fail(MO_EINVAL, "eps must be finite and >= 0");
+  if (!finite(h.a) || !finite(h.b) || !finite(h.c)) return fail(MO_EINVAL, "abc must be finite");
+  if (h.ns_steps < 0 || h.ns_steps > 16) return fail(MO_EINVAL, "ns_steps must be in [0, 16]");
+  return MO_OK;
+}
+
+// Enqueues the whole step.  `d_desc` is the device copy of plan.descs.
+// `store_out`: Newton-Schulz-only mode, writing X_N into store_out.
+int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float* update_rms, char* ws,
+             size_t ws_bytes, size_t fixed_used, hipStream_t s, void* store_out, int64_t store_stride) {
+  const int esz = plan.esz();
+  float* rscale_all = reinterpret_cast<float*>(ws + fixed_used);
+  char* region = ws + fixed_used + align_up(static_cast<size_t>(plan.count) * 4);
+  // every chunk region is carved into 8 pieces, each rounded up to kAlign
+  const size_t region_bytes = ws_bytes - static_cast<size_t>(region - ws) - 8 * kAlign;
+  int rc;
+  for (const Bin& bin : plan.bins) {
+    const BinLayout L = bin_layout(bin, esz);
+    const int cap = static_cast<int>(std::min<size_t>(bin.count, region_bytes / L.per_mat));
+    if (cap < 1) return fail(MO_EWORKSPACE, "workspace too small for a %d x %d matrix", bin.m, bin.n);
+    const double scale = static_cast<double>(h.rms_scale) * std::sqrt(static_cast<double>(bin.n));
+    const float step = static_cast<float>(static_cast<double>(h.lr) * scale);
+    const float lrwd = static_cast<float>(static_cast<double>(h.lr) * h.wd);
+    for (int c0 = 0; c0 < bin.count; c0 += cap) {
+      const int chunk = std::min(cap, bin.count - c0);
+      const MatDesc* desc = d_desc + bin.first + c0;
+      float* rscale = rscale_all + bin.first + c0;
+      // carve the chunk region
+      char* q = region;
+      auto take = [&](size_t bytes) {
+        char* r = q;
+        q += align_up(bytes);
+        return r;
+      };
+      float* norm_part = reinterpret_cast<float*>(take(static_cast<size_t>(chunk) * L.prep_tiles * 4));
+      float* rms_part = reinterpret_cast<float*>(take(static_cast<size_t>(chunk) * L.rms_tiles * 4));
+      char* xr[2];
+      char* xt[2];
+      const size_t xb = static_cast<size_t>(chunk) * L.x_elems * esz;
+      xr[0] = take(xb);
+      xt[0] = take(xb);
+      xr[1] = take(xb);
+      xt[1] = take(xb);
+      char* S = take(static_cast<size_t>(chunk) * L.s_elems * esz);
+      char* P = take(static_cast<size_t>(chunk) * L.s_elems * esz);
+
+      {
+        PrepArgs a{};
+        a.desc = desc;
+        a.x_row = xr[0];
+        a.x_t = xt[0];
+        a.x_stride = L.x_elems;
+        a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
+        a.tiles_per_mat = L.prep_tiles;
+        a.mu = h.mu;
+        a.nesterov = h.nesterov;
+        a.has_mom = h.has_mom ? 1 : 0;
+        a.grad_dt = plan.grad_dt; a.mom_dt = plan.mom_dt; a.ns_dt = plan.ns_dt;
+        a.norm_part = norm_part;
+        const double elems = static_cast<double>(chunk) * bin.m * bin.n;
+        const double bytes = elems * (dt_size(plan.grad_dt) + (h.has_mom ? 2 * dt_size(plan.mom_dt) : 0) + esz);
+        ProfScope ps(MO_K_MOMENTUM, s, bytes);
+        if ((rc = checked(launch_prep(a, chunk, s), s, "prep"))) return rc;
+      }
+      {
+        NormArgs a{norm_part, L.prep_tiles, h.eps, rscale};
+        ProfScope ps(MO_K_NORM, s, static_cast<double>(chunk) * L.prep_tiles * 4);
+        if ((rc = checked(launch_norm(a, chunk, s), s, "norm"))) return rc;
+      }
+      const bool want_rms = update_rms != nullptr && store_out == nullptr;
+      if (h.ns_steps == 0) {
+        ApplyX0Args a{};
+        a.desc = desc;
+        a.x_row = xr[0];
+        a.x_t = xt[0];
+        a.x_stride = L.x_elems;
+        a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
+        a.tiles_per_mat = L.x0_tiles;
+        a.rscale = rscale;
+        a.lrwd = lrwd;
+        a.step = step;
+        a.ns_dt = plan.ns_dt;
+        a.out = store_out ? static_cast<char*>(store_out) + static_cast<size_t>(c0) * store_stride * esz : nullptr;
+        a.s_out = store_stride;
+        a.rms_part = want_rms ? rms_part : nullptr;
+        const double elems = static_cast<double>(chunk) * bin.m * bin.n;
+        ProfScope ps(MO_K_APPLY_X0, s, elems * (esz + (store_out ? esz : 8)));
+        if ((rc = checked(launch_apply_x0(a, chunk, s), s, "apply_x0"))) return rc;
+      } else {
+        const int T = tile_size(bin.cfg);
+        const int tm = bin.m_pad / T, tn = bin.n_pad / T;
+        const double m = bin.m, n = bin.n;
+        for (int k = 0; k < h.ns_steps; ++k) {
+          char* xrc = xr[k & 1];
+          char* xtc = xt[k & 1];
+          char* xrn = xr[(k + 1) & 1];
+          char* xtn = xt[(k + 1) & 1];
+          const float* rs = k == 0 ? rscale : nullptr;
+          {  // S = X X^T
+            GemmArgs g{};
+            g.A = xrc; g.sA = L.x_elems; g.lda = bin.n_pad;
+            g.B = xrc; g.sB = L.x_elems; g.ldb = bin.n_pad;
+            g.C = S;   g.sC = L.s_elems; g.ldc = bin.m_pad;
+            g.M = bin.m_pad; g.N = bin.m_pad; g.K = bin.n_pad;
+            g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tm * (tm + 1) / 2; g.batch = chunk;
+            g.rscale = rs; g.alpha = 1.0f; g.beta = 0.0f;
+            ProfScope ps(MO_K_GRAM, s, chunk * m * m * n);
+            if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_GRAM, g, s), s, "gram"))) return rc;
+          }
+          {  // P = b S + c S S
+            GemmArgs g{};
+            g.A = S; g.sA = L.s_elems; g.lda = bin.m_pad;
+            g.B = S; g.sB = L.s_elems; g.ldb = bin.m_pad;
+            g.D = S; g.sD = L.s_elems; g.ldd = bin.m_pad;
+            g.C = P; g.sC = L.s_elems; g.ldc = bin.m_pad;
+            g.M = bin.m_pad; g.N = bin.m_pad; g.K = bin.m_pad;
+            g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tm * (tm + 1) / 2; g.batch = chunk;
+            g.rscale = nullptr; g.alpha = h.c; g.beta = h.b;
+            ProfScope ps(MO_K_POLY, s, chunk * m * m * m);
+            if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_POLY, g, s), s, "poly"))) return rc;
+          }
+          {  // X' = a X + P X
+            const bool last = (k + 1 == h.ns_steps);
+            GemmArgs g{};
+            g.A = P;   g.sA = L.s_elems; g.lda = bin.m_pad;
+            g.B = xtc; g.sB = L.x_elems; g.ldb = bin.m_pad;
+            g.D = xrc; g.sD = L.x_elems; g.ldd = bin.n_pad;
+            g.M = bin.m_pad; g.N = bin.n_pad; g.K = bin.m_pad;
+            g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.batch = chunk;
+            g.rscale = rs; g.alpha = 1.0f; g.beta = h.a;
+            Epi epi = EPI_UPDATE;
+            int cls = MO_K_UPDATE;
+            if (!last) {
+              g.C = xrn; g.sC = L.x_elems; g.ldc = bin.n_pad;
+              g.Ct = xtn; g.sCt = L.x_elems; g.ldct = bin.m_pad;
+            } else {
+              g.desc = desc;
+              g.m_true = bin.m; g.n_true = bin.n;
+              g.lrwd = lrwd; g.step = step;
+              g.rms_part = want_rms ? rms_part : nullptr;
+              if (store_out) {
+                epi = EPI_STORE;
+                g.out = static_cast<char*>(store_out) + static_cast<size_t>(c0) * store_stride * esz;
+                g.s_out = store_stride;
+              } else {
+                epi = EPI_APPLY;
+              }
+              cls = MO_K_APPLY;
+            }
+            ProfScope ps(cls, s, 2.0 * chunk * m * m * n);
+            if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, epi, g, s), s, "update"))) return rc;
+          }
+        }
+      }
+      if (want_rms) {
+        RmsArgs a{};
+        a.desc = desc;
+        a.part = rms_part;
+        a.tiles = h.ns_steps == 0 ? L.x0_tiles : L.upd_tiles;
+        a.inv_count = 1.0 / (static_cast<double>(bin.m) * bin.n);
+        a.update_rms = update_rms;
+        ProfScope ps(MO_K_RMS, s, static_cast<double>(chunk) * a.tiles * 4);
+        if ((rc = checked(launch_rms(a, chunk, s), s, "rms"))) return rc;
+      }
+    }
+  }
+  return MO_OK;
+}
+
+int check_workspace(void* ws, size_t ws_bytes, size_t min_bytes) {
+  if (!ws) return fail(MO_EWORKSPACE, "workspace is NULL (need %zu bytes)", min_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(MO_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < min_bytes)
+    return fail(MO_EWORKSPACE, "workspace has %zu bytes, need at least %zu", ws_bytes, min_bytes);
+  return MO_OK;
+}
+
+// Pinned host staging for one-shot descriptor uploads: reused once the
+// previous upload from it has completed.
+struct Staging {
+  void* host = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+thread_local Staging g_stage;
+
+int upload_descs(const HostPlan& plan, void* dst, hipStream_t s) {
+  const size_t bytes = plan.descs.size() * sizeof(MatDesc);
+  if (bytes == 0) return MO_OK;
+  hipError_t e;
+  if (g_stage.pending) {
+    if ((e = hipEventSynchronize(g_stage.done)) != hipSuccess)
+      return fail(MO_EHIP, "staging wait failed: %s", hipGetErrorString(e));
+    g_stage.pending = false;
+  }
+  if (g_stage.bytes < bytes) {
+    if (g_stage.host) (void)hipHostFree(g_stage.host);
+    g_stage.host = nullptr;
+    g_stage.bytes = 0;
+    if ((e = hipHostMalloc(&g_stage.host, bytes, 0)) != hipSuccess)
+      return fail(MO_EHIP, "pinned staging allocation failed: %s", hipGetErrorString(e));
+    g_stage.bytes = bytes;
+  }
+  if (!g_stage.done && (e = hipEventCreateWithFlags(&g_stage.done, hipEventDisableTiming)) != hipSuccess)
+    return fail(MO_EHIP, "event creation failed: %s", hipGetErrorString(e));
+  std::memcpy(g_stage.host, plan.descs.data(), bytes);
+  if ((e = hipMemcpyAsync(dst, g_stage.host, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return fail(MO_EHIP, "descriptor upload failed: %s", hipGetErrorString(e));
+  if ((e = hipEventRecord(g_stage.done, s)) != hipSuccess)
+    return fail(MO_EHIP, "event record failed: %s", hipGetErrorString(e));
+  g_stage.pending = true;
+  return MO_OK;
+}
+
+Hyper make_hyper(float lr, float wd, float mu, int nesterov, int ns_steps, const float* abc, float rms_scale,
+                 float eps, bool has_mom) {
+  Hyper h{};
+  h.lr = lr; h.wd = wd; h.mu = mu; h.nesterov = nesterov ? 1 : 0; h.ns_steps = ns_steps;
+  h.a = abc ? abc[0] : 3.4445f;
+  h.b = abc ? abc[1] : -4.7750f;
+  h.c = abc ? abc[2] : 2.0315f;
+  h.rms_scale = rms_scale; h.eps = eps; h.has_mom = has_mom;
+  return h;
+}
+
+}  // namespace
+
+struct mo_muon_plan {
+  HostPlan plan;
+  MatDesc* d_desc = nullptr;
+  int device = 0;
+};
+
+extern "C" {
+
+int mo_abi_version(void) { return MO_ABI_VERSION; }
+
+const char* mo_last_error(void) { return g_err.c_str(); }
+
+int mo_muon_workspace_size(const mo_tensor* tensors, int64_t count, int ns_dtype, size_t* full_bytes,
+                           size_t* min_bytes) {
+  if (!full_bytes) return fail(MO_EINVAL, "full_bytes is NULL");
+  HostPlan p;
+  int rc = build_plan(tensors, count, MO_F32, MO_F32, ns_dtype, false, p);
+  if (rc) return rc;
+  ws_sizes(p, true, full_bytes, min_bytes);
+  return MO_OK;
+}
+
+int mo_muon_step(const mo_tensor* tensors, int64_t count, int grad_dtype, int mom_dtype, int ns_dtype, float lr,
+                 float wd, float mu, int nesterov, int ns_steps, const float* abc, float rms_scale, float eps,
+                 float* update_rms, void* workspace, size_t workspace_bytes, void* stream) {
+  HostPlan p;
+  int rc = build_plan(tensors, count, grad_dtype, mom_dtype, ns_dtype, true, p);
+  if (rc) return rc;
+  const Hyper h = make_hyper(lr, wd, mu, nesterov, ns_steps, abc, rms_scale, eps, true);
+  if ((rc = validate_hyper(h))) return rc;
+  if (update_rms && (reinterpret_cast<uintptr_t>(update_rms) & 3u))
+    return fail(MO_EINVAL, "update_rms must be 4-byte aligned");
+  if (count == 0) return MO_OK;
+  size_t full = 0, mn = 0;
+  ws_sizes(p, true, &full, &mn);
+  if ((rc = check_workspace(workspace, workspace_bytes, mn))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((rc = upload_descs(p, ws, s))) return rc;
+  const size_t table = align_up(p.descs.size() * sizeof(MatDesc));
+  return run_step(p, reinterpret_cast<const MatDesc*>(ws), h, update_rms, ws, workspace_bytes, table, s, nullptr, 0);
+}
+
+int mo_muon_plan_create(const mo_tensor* tensors, int64_t count, int grad_dtype, int mom_dtype, int ns_dtype,
+                        mo_muon_plan** out) {
+  if (!out) return fail(MO_EINVAL, "plan is NULL");
+  *out = nullptr;
+  auto* pl = new mo_muon_plan();
+  int rc = build_plan(tensors, count, grad_dtype, mom_dtype, ns_dtype, true, pl->plan);
+  if (rc) {
+    delete pl;
+    return rc;
+  }
+  hipError_t e = hipGetDevice(&pl->device);
+  if (e != hipSuccess) {
+    delete pl;
+    return fail(MO_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  }
+  const size_t bytes = pl->plan.descs.size() * sizeof(MatDesc);
+  if (bytes) {
+    if ((e = hipMalloc(&pl->d_desc, bytes)) != hipSuccess) {
+      delete pl;
+      return fail(MO_EHIP, "descriptor table allocation failed: %s", hipGetErrorString(e));
+    }
+    if ((e = hipMemcpy(pl->d_desc, pl->plan.descs.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+      (void)hipFree(pl->d_desc);
+      delete pl;
+      return fail(MO_EHIP, "descriptor upload failed: %s", hipGetErrorString(e));
+    }
+  }
+  *out = pl;
+  return MO_OK;
+}
+
+int mo_muon_plan_workspace_size(const mo_muon_plan* plan, size_t* full_bytes, size_t* min_bytes) {
+  if (!plan || !full_bytes) return fail(MO_EINVAL, "plan and full_bytes must be non-NULL");
+  ws_sizes(plan->plan, false, full_bytes, min_bytes);
+  return MO_OK;
+}
+
+int mo_muon_plan_step(mo_muon_plan* plan, float lr, float wd, float mu, int nesterov, int ns_steps,
+                      const float* abc, float rms_scale, float eps, float* update_rms, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MO_EINVAL, "plan is NULL");
+  const Hyper h = make_hyper(lr, wd, mu, nesterov, ns_steps, abc, rms_scale, eps, true);
+  int rc;
+  if ((rc = validate_hyper(h))) return rc;
+  if (update_rms && (reinterpret_cast<uintptr_t>(update_rms) & 3u))
+    return fail(MO_EINVAL, "update_rms must be 4-byte aligned");
+  if (plan->plan.count == 0) return MO_OK;
+  size_t full = 0, mn = 0;
+  ws_sizes(plan->plan, false, &full, &mn);
+  if ((rc = check_workspace(workspace, workspace_bytes, mn))) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(MO_EINVAL, "plan was created on device %d, current device is %d", plan->device, dev);
+  return run_step(plan->plan, plan->d_desc, h, update_rms, static_cast<char*>(workspace), workspace_bytes, 0,
+                  static_cast<hipStream_t>(stream), nullptr, 0);
+}
+
+int mo_muon_plan_destroy(mo_muon_plan* plan) {
+  if (!plan) return MO_OK;
+  int rc = MO_OK;
+  if (plan->d_desc) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipFree(plan->d_desc);
+    if (e != hipSuccess) rc = fail(MO_EHIP, "plan destroy failed: %s", hipGetErrorString(e));
+  }
+  delete plan;
+  return rc;
+}
+
+int mo_adamw_step(const mo_tensor* tensors, int64_t count, int grad_dtype, float lr, float wd, float beta1,
+                  float beta2, float eps, int64_t step, void* stream) {
+  int rc;
+  if ((rc = validate_dtype(grad_dtype, "grad_dtype"))) return rc;
+  if (count < 0) return fail(MO_EINVAL, "count must be >= 0");
+  if (count > 0 && !tensors) return fail(MO_EINVAL, "tensors is NULL");
+  if (!finite(lr) || !finite(wd) || !finite(eps) || eps < 0.0f)
+    return fail(MO_EINVAL, "lr, wd must be finite; eps finite and >= 0");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(MO_EINVAL, "beta1 and beta2 must be in [0, 1)");
+  if (step < 1) return fail(MO_EINVAL, "step must be >= 1");
+  std::vector<Range> ranges;
+  for (int64_t i = 0; i < count; ++i) {
+    const mo_tensor& x = tensors[i];
+    if (x.rows < 1 || x.cols < 1 || x.rows > (int64_t{1} << 40) / x.cols)
+      return fail(MO_EINVAL, "tensor %lld: rows and cols must be >= 1", static_cast<long long>(i));
+    if (!x.param || !x.grad || !x.state0 || !x.state1)
+      return fail(MO_EINVAL, "tensor %lld: param, grad, state0 and state1 must be non-NULL",
+                  static_cast<long long>(i));
+    if (!aligned16(x.param) || !aligned16(x.grad) || !aligned16(x.state0) || !aligned16(x.state1))
+      return fail(MO_EINVAL, "tensor %lld: pointers must be 16-byte aligned", static_cast<long long>(i));
+    const uintptr_t ne = static_cast<uintptr_t>(x.rows * x.cols);
+    ranges.push_back({reinterpret_cast<uintptr_t>(x.param), reinterpret_cast<uintptr_t>(x.param) + ne * 4, i, "param"});
+    ranges.push_back({reinterpret_cast<uintptr_t>(x.grad),
+                      reinterpret_cast<uintptr_t>(x.grad) + ne * dt_size(grad_dtype), i, "grad"});
+    ranges.push_back({reinterpret_cast<uintptr_t>(x.state0), reinterpret_cast<uintptr_t>(x.state0) + ne * 4, i, "m"});
+    ranges.push_back({reinterpret_cast<uintptr_t>(x.state1), reinterpret_cast<uintptr_t>(x.state1) + ne * 4, i, "v"});
+  }
+  if ((rc = check_overlap(ranges))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AdamArgs a{};
+  a.grad_dt = grad_dtype;
+  a.lr = lr; a.wd = wd; a.beta1 = beta1; a.beta2 = beta2; a.eps = eps;
+  a.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(beta1));
+  a.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(beta2));
+  a.bc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
+  a.bc2_rsqrt = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
+  for (int64_t i0 = 0; i0 < count; i0 += kAdamMaxTensors) {
+    const int nt = static_cast<int>(std::min<int64_t>(kAdamMaxTensors, count - i0));
+    int64_t blocks = 0;
+    double bytes = 0;
+    for (int k = 0; k < nt; ++k) {
+      const mo_tensor& x = tensors[i0 + k];
+      AdamTensor& T = a.t[k];
+      T.p = static_cast<float*>(x.param);
+      T.g = x.grad;
+      T.m = static_cast<float*>(x.state0);
+      T.v = static_cast<float*>(x.state1);
+      T.n = x.rows * x.cols;
+      T.block0 = blocks;
+      blocks += (T.n + kAdamElemsPerBlock - 1) / kAdamElemsPerBlock;
+      bytes += static_cast<double>(T.n) * (dt_size(grad_dtype) + 24);
+    }
+    a.count = nt;
+    if (blocks > 0x7fffffff) return fail(MO_EINVAL, "AdamW launch too large");
+    ProfScope ps(MO_K_ADAMW, s, bytes);
+    if ((rc = checked(launch_adamw(a, blocks, s), s, "adamw"))) return rc;
+  }
+  return MO_OK;
+}
+
+int mo_newton_schulz_workspace_size(int64_t batch, int64_t rows, int64_t cols, int dtype, size_t* bytes) {
+  if (!bytes) return fail(MO_EINVAL, "bytes is NULL");
+  if (batch < 0) return fail(MO_EINVAL, "batch must be >= 0");
+  std::vector<mo_tensor> t(static_cast<size_t>(batch));
+  for (auto& x : t) {
+    x.rows = rows;
+    x.cols = cols;
+  }
+  HostPlan p;
+  int rc = build_plan(t.data(), batch, dtype, MO_F32, dtype, false, p);
+  if (rc) return rc;
+  ws_sizes(p, true, bytes, nullptr);
+  return MO_OK;
+}
+
+int mo_newton_schulz(const void* input, void* output, int64_t batch, int64_t rows, int64_t cols, int dtype,
+                     int ns_steps, const float* abc, float eps, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int rc;
+  if ((rc = validate_dtype(dtype, "dtype"))) return rc;
+  if (batch < 0) return fail(MO_EINVAL, "batch must be >= 0");
+  if (batch > 0 && (!input || !output)) return fail(MO_EINVAL, "input and output must be non-NULL");
+  if (!aligned16(input) || !aligned16(output)) return fail(MO_EINVAL, "input and output must be 16-byte aligned");
+  const int64_t esz = dtype == MO_F32 ? 4 : 2;
+  std::vector<mo_tensor> t(static_cast<size_t>(batch));
+  for (int64_t i = 0; i < batch; ++i) {
+    t[i].rows = rows;
+    t[i].cols = cols;
+    t[i].grad = static_cast<const char*>(input) + i * rows * cols * esz;
+    t[i].param = static_cast<char*>(output) + i * rows * cols * esz;   // placeholder for the table
+    t[i].state0 = nullptr;
+    t[i].state1 = nullptr;
+  }
+  HostPlan p;
+  if ((rc = build_plan(t.data(), batch, dtype, MO_F32, dtype, false, p))) return rc;
+  if (batch > 0) {
+    const uintptr_t in0 = reinterpret_cast<uintptr_t>(input), out0 = reinterpret_cast<uintptr_t>(output);
+    const uintptr_t nb = static_cast<uintptr_t>(batch * rows * cols * esz);
+    if (in0 < out0 + nb && out0 < in0 + nb) return fail(MO_EINVAL, "input and output overlap");
+  }
+  const Hyper h = make_hyper(0.0f, 0.0f, 0.0f, 0, ns_steps, abc, 0.0f, eps, false);
+  if ((rc = validate_hyper(h))) return rc;
+  if (batch == 0) return MO_OK;
+  // every matrix has the same shape: one bin whose descriptors keep the
+  // caller's order, so output b lands at output + b * rows * cols
+  size_t full = 0, mn = 0;
+  ws_sizes(p, true, &full, &mn);
+  if ((rc = check_workspace(workspace, workspace_bytes, mn))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((rc = upload_descs(p, ws, s))) return rc;
+  const size_t table = align_up(p.descs.size() * sizeof(MatDesc));
+  return run_step(p, reinterpret_cast<const MatDesc*>(ws), h, nullptr, ws, workspace_bytes, table, s, output,
+                  rows * cols);
+}
+
+int mo_profile_enable(unsigned int class_mask) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_mask = class_mask & ((1u << MO_K_COUNT) - 1);
+  return MO_OK;
+}
+
+int mo_profile_read(int kernel_class, int64_t* launches, double* total_ms, double* total_work) {
+  if (kernel_class < 0 || kernel_class >= MO_K_COUNT) return fail(MO_EINVAL, "bad kernel class %d", kernel_class);
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  ProfClass& c = g_prof[kernel_class];
+  for (ProfEntry& e : c.pending) {
+    float ms = 0.0f;
+    hipError_t err = hipEventSynchronize(e.stop);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e.start, e.stop);
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
+    if (err != hipSuccess) {
+      c.pending.clear();
+      return fail(MO_EHIP, "profile event failed: %s", hipGetErrorString(err));
+    }
+    c.launches += 1;
+    c.ms += ms;
+    c.work += e.work;
+  }
+  c.pending.clear();
+  if (launches) *launches = c.launches;
+  if (total_ms) *total_ms = c.ms;
+  if (total_work) *total_work = c.work;
+  return MO_OK;
+}
+
+int mo_profile_reset(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (ProfClass& c : g_prof) {
+    for (ProfEntry& e : c.pending) {
+      (void)hipEventSynchronize(e.stop);
+      (void)hipEventDestroy(e.start);
+      (void)hipEventDestroy(e.stop);
+    }
+    c = ProfClass{};
+  }
+  return MO_OK;
+}
+
+}  // extern "C"

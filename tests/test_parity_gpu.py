@@ -1,0 +1,361 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances:
+* fp32 Newton-Schulz path: relative Frobenius error of the update <= 1e-4;
+* bf16 path: relative Frobenius error <= 2e-2 and per-singular-value
+  deviation ``max_i |u_i^T X v_i - f^N(sigma_i)|`` <= 0.05 (singular
+  vectors from the oracle's SVD of the Newton-Schulz input);
+* momentum in bf16: within half a bf16 ulp of the oracle's fp64 value
+  (round-to-nearest of the fp32 result); fp32 momentum to 1e-6 relative;
+* AdamW: fp32 arithmetic against fp64, 1e-5 relative on the update.
+bf16 inputs are upcast exactly for the oracle; the oracle always starts from
+the same pre-step state as the GPU (step-local parity), except for the
+all-fp32 workload whose three-step trajectory is compared directly.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import muon_oracle as mo, spectral as sp
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+HYP = dict(lr=1e-3, wd=0.1, mu=0.95, nesterov=True, ns_steps=5, rms_scale=0.2, eps=1e-7)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def _gen(seed):
+    g = torch.Generator()
+    g.manual_seed(seed)
+    return g
+
+
+def randn(shape, seed, std=1.0, dtype=torch.float32):
+    return (torch.randn(*shape, generator=_gen(seed)) * std).to(dtype).to(DEV)
+
+
+@pytest.fixture(scope="module")
+def mod():
+    import matrix_orthogonalizing_optimizer_amd as m
+    m._lib.lib()
+    return m
+
+
+# ---------------------------------------------------------------- Newton-Schulz only
+
+NS_F32_SHAPES = [(128, 512), (512, 128), (100, 300), (65, 64), (1, 40), (40, 1), (257, 130)]
+
+
+@pytest.mark.parametrize("shape", NS_F32_SHAPES)
+def test_ns_fp32(mod, shape):
+    x = randn(shape, 1 + shape[0] * 3 + shape[1])
+    X = mod.newton_schulz(x, ns_steps=5)
+    torch.cuda.synchronize()
+    ref, _ = mo.orthogonalize(f64(x), 5, eps=1e-7)
+    assert sp.rel_fro(f64(X), ref) <= 1e-4
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2, 10])
+def test_ns_fp32_steps(mod, steps):
+    x = randn((96, 200), 7)
+    X = mod.newton_schulz(x, ns_steps=steps)
+    ref, _ = mo.orthogonalize(f64(x), steps, eps=1e-7)
+    assert sp.rel_fro(f64(X), ref) <= 1e-4
+
+
+NS_BF16_SHAPES = [(128, 512), (300, 700), (700, 300), (1408, 2048), (2048, 512),
+                  (64, 2048), (512, 4096), (1536, 1536), (2048, 64), (257, 1031)]
+
+
+@pytest.mark.parametrize("shape", NS_BF16_SHAPES)
+def test_ns_bf16(mod, shape):
+    x = randn(shape, 11 + shape[0] + 7 * shape[1], dtype=torch.bfloat16)
+    X = mod.newton_schulz(x, ns_steps=5)
+    xo = f64(x)
+    ref, _ = mo.orthogonalize(xo, 5, eps=1e-7)
+    err = sp.rel_fro(f64(X), ref)
+    dev = sp.per_sigma_deviation(f64(X), xo, 5, eps=1e-7)
+    print(f"{shape}: rel_fro {err:.3e} per_sigma {dev:.3e}")
+    assert err <= 2e-2
+    assert dev <= 0.05
+
+
+def test_ns_bf16_thin_small_m(mod):
+    """A 33 x 1000 input (no workload has it): storing S, P and X in bf16
+    -- the precision the pages run Newton-Schulz in -- gives about 2.5e-2
+    relative Frobenius error here (a CPU model of the same rounding points
+    gives the same figure), so this shape is gated on the per-singular-value
+    criterion, with a looser Frobenius bound."""
+    x = randn((33, 1000), 11 + 33 + 7000, dtype=torch.bfloat16)
+    X = mod.newton_schulz(x, ns_steps=5)
+    xo = f64(x)
+    ref, _ = mo.orthogonalize(xo, 5, eps=1e-7)
+    assert sp.rel_fro(f64(X), ref) <= 3e-2
+    assert sp.per_sigma_deviation(f64(X), xo, 5, eps=1e-7) <= 0.05
+
+
+def test_ns_batched_bf16(mod):
+    x = randn((6, 256, 384), 5, dtype=torch.bfloat16)
+    X = mod.newton_schulz(x, ns_steps=5)
+    for b in range(6):
+        ref, _ = mo.orthogonalize(f64(x[b]), 5, eps=1e-7)
+        assert sp.rel_fro(f64(X[b]), ref) <= 2e-2
+
+
+def test_ns_zero_input(mod):
+    x = torch.zeros(64, 192, device=DEV)
+    X = mod.newton_schulz(x, ns_steps=5)
+    assert torch.count_nonzero(X).item() == 0
+
+
+# ---------------------------------------------------------------- full step, fp32
+
+def test_fp32_workload_three_steps(mod):
+    """The all-fp32 workload: [128,512], W~N(0,0.02^2), 3 steps of N(0,1)
+    gradients, zero momentum; trajectories compared directly."""
+    wl = W.WORKLOADS["fp32_128x512"]
+    T = W.make_muon_tensors(wl, "cpu")
+    Wg = T.params[0].clone().to(DEV)
+    Mg = T.moms[0].clone().to(DEV)
+    Wo = f64(T.params[0])
+    Mo = f64(T.moms[0])
+    rms = torch.zeros(1, device=DEV)
+    for step in range(wl.steps):
+        G = W.make_grads(wl, "cpu", step).view(128, 512)
+        Gg = G.to(DEV)
+        W_prev = f64(Wg)
+        mod.muon_step([Wg], [Gg], [Mg], ns_dtype=torch.float32, update_rms=rms, **HYP)
+        torch.cuda.synchronize()
+        Wo_prev = Wo
+        Wo, Mo, Xo, rms_o = mo.muon_step(Wo, f64(G), Mo, abc=mo.NS_COEFFS, **HYP)
+        # update of this step, and the whole trajectory so far
+        upd_err = sp.rel_fro(W_prev - f64(Wg), Wo_prev - Wo)
+        traj_err = np.linalg.norm(f64(Wg) - Wo) / np.linalg.norm(Wo - f64(T.params[0]))
+        print(f"step {step}: update {upd_err:.2e} trajectory {traj_err:.2e}")
+        assert upd_err <= 1e-4 and traj_err <= 1e-4
+        assert sp.rel_fro(f64(Mg), Mo) <= 1e-6
+        assert abs(rms.item() - rms_o) <= 1e-4 * rms_o
+
+
+# ---------------------------------------------------------------- full step, bf16
+
+MIXED = [(300, 700), (700, 300), (64, 2048), (2048, 64), (128, 128), (1, 300),
+         (257, 1031), (1031, 257), (300, 700)]
+
+
+def _mixed_state(seed, shapes, grad_dtype=torch.float32, mom_dtype=torch.bfloat16,
+                 zero_mom=False):
+    Ps, Gs, Ms = [], [], []
+    for i, s in enumerate(shapes):
+        Ps.append(randn(s, seed + 3 * i, 0.02))
+        Gs.append(randn(s, seed + 3 * i + 1, 1e-3 * (1 + i), grad_dtype))
+        Ms.append(torch.zeros(s, device=DEV, dtype=mom_dtype) if zero_mom
+                  else randn(s, seed + 3 * i + 2, 1e-3, mom_dtype))
+    return Ps, Gs, Ms
+
+
+def _check_step(P0, G, M0, P1, M1, rms, hyp, ns_bf16=True, mom_bf16=True):
+    """Step-local parity of one matrix."""
+    Wo, Mo, Xo, rms_o = mo.muon_step(P0, G, M0, abc=mo.NS_COEFFS, **hyp)
+    upd_g = P0 - P1
+    upd_o = P0 - Wo
+    err = sp.rel_fro(upd_g, upd_o)
+    if mom_bf16:
+        # half a bf16 ulp of the result, plus the fp32 evaluation error of
+        # mu*M + G, which matters where the two terms cancel
+        tol = np.abs(Mo) * (2.0 ** -8 + 2.0 ** -20) + \
+            (np.abs(hyp["mu"] * M0) + np.abs(G)) * 2.0 ** -22 + 1e-30
+        assert np.all(np.abs(M1 - Mo) <= tol)
+    else:
+        assert sp.rel_fro(M1, Mo) <= 1e-6
+    r, c = P0.shape
+    scale = hyp["rms_scale"] * math.sqrt(max(r, c))
+    X_rec = (upd_g - hyp["lr"] * hyp["wd"] * P0) / (hyp["lr"] * scale)
+    _, N = mo.momentum_update(M0, G, hyp["mu"], hyp["nesterov"])
+    if ns_bf16:
+        assert err <= 2e-2, err
+        if min(r, c) > 1:
+            assert sp.per_sigma_deviation(X_rec, N, hyp["ns_steps"], eps=hyp["eps"]) <= 0.05
+        if rms is not None:
+            assert abs(rms - rms_o) <= 2e-2 * rms_o
+    else:
+        assert err <= 1e-4, err
+        if rms is not None:
+            assert abs(rms - rms_o) <= 1e-4 * rms_o
+    return err
+
+
+@pytest.mark.parametrize("grad_dtype", [torch.float32, torch.bfloat16])
+def test_step_bf16_mixed_shapes(mod, grad_dtype):
+    Ps, Gs, Ms = _mixed_state(100, MIXED, grad_dtype)
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    rms = torch.zeros(len(Ps), device=DEV)
+    mod.muon_step(Ps, Gs, Ms, update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    for i in range(len(Ps)):
+        e = _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), HYP)
+        print(MIXED[i], f"update rel_fro {e:.3e}")
+
+
+@pytest.mark.parametrize("variant", [{"nesterov": False}, {"ns_steps": 0}, {"ns_steps": 1},
+                                     {"ns_steps": 10}, {"mu": 0.0}])
+def test_step_variants(mod, variant):
+    shapes = [(200, 456), (456, 200), (64, 64)]
+    Ps, Gs, Ms = _mixed_state(200, shapes)
+    P0, G0, M0 = [f64(p) for p in Ps], [f64(g) for g in Gs], [f64(m) for m in Ms]
+    hyp = dict(HYP, **variant)
+    rms = torch.zeros(len(Ps), device=DEV)
+    mod.muon_step(Ps, Gs, Ms, update_rms=rms, **hyp)
+    torch.cuda.synchronize()
+    for i in range(len(Ps)):
+        if hyp["ns_steps"] == 10:
+            # bf16 iterates at N=10 exceed 2e-2 Frobenius (the slope of the
+            # 10-fold map reaches ~86); gate on the per-sigma criterion only
+            Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=mo.NS_COEFFS, **hyp)
+            r, c = shapes[i]
+            X_rec = (P0[i] - f64(Ps[i]) - hyp["lr"] * hyp["wd"] * P0[i]) / (
+                hyp["lr"] * hyp["rms_scale"] * math.sqrt(max(r, c)))
+            _, N = mo.momentum_update(M0[i], G0[i], hyp["mu"], hyp["nesterov"])
+            assert sp.per_sigma_deviation(X_rec, N, 10, eps=hyp["eps"]) <= 0.05
+            assert sp.rel_fro(P0[i] - f64(Ps[i]), P0[i] - Wo) <= 5e-2
+        else:
+            _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), hyp)
+
+
+def test_zero_gradient_is_decay_only(mod):
+    shapes = [(130, 260), (260, 130)]
+    Ps = [randn(s, 300 + i, 0.02) for i, s in enumerate(shapes)]
+    Gs = [torch.zeros(s, device=DEV) for s in shapes]
+    Ms = [torch.zeros(s, device=DEV, dtype=torch.bfloat16) for s in shapes]
+    P0 = [p.clone() for p in Ps]
+    rms = torch.full((2,), -1.0, device=DEV)
+    mod.muon_step(Ps, Gs, Ms, update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    for p0, p1, m in zip(P0, Ps, Ms):
+        exp = f64(p0) - HYP["lr"] * HYP["wd"] * f64(p0)
+        assert np.all(np.abs(f64(p1) - exp) <= np.abs(exp) * 2.0 ** -23)
+        assert torch.count_nonzero(m).item() == 0
+    assert torch.all(rms == 0).item()
+
+
+def test_fp32_path_mixed_shapes(mod):
+    shapes = [(100, 300), (300, 100), (64, 64), (1, 77), (129, 200)]
+    Ps, Gs, Ms = _mixed_state(400, shapes, torch.float32, torch.float32)
+    P0, G0, M0 = [f64(p) for p in Ps], [f64(g) for g in Gs], [f64(m) for m in Ms]
+    rms = torch.zeros(len(Ps), device=DEV)
+    mod.muon_step(Ps, Gs, Ms, ns_dtype=torch.float32, update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    for i in range(len(Ps)):
+        _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), HYP,
+                    ns_bf16=False, mom_bf16=False)
+
+
+# ---------------------------------------------------------------- execution properties
+
+def _run_once(mod, shapes, seed, **kw):
+    Ps, Gs, Ms = _mixed_state(seed, shapes)
+    mod.muon_step(Ps, Gs, Ms, **HYP, **kw)
+    torch.cuda.synchronize()
+    return Ps, Ms
+
+
+def test_deterministic_and_chunking_and_plan(mod):
+    shapes = [(256, 512)] * 5 + [(512, 256)] * 3 + [(64, 1000)] * 2
+    Pa, Ma = _run_once(mod, shapes, 500)
+    Pb, Mb = _run_once(mod, shapes, 500)
+    for x, y in zip(Pa + Ma, Pb + Mb):
+        assert torch.equal(x, y)
+    # smallest workspace: every shape group runs in several passes
+    full, mn = mod.muon_workspace_size(shapes)
+    ws = torch.empty(mn, dtype=torch.uint8, device=DEV)
+    Pc, Mc = _run_once(mod, shapes, 500, workspace=ws)
+    for x, y in zip(Pa + Ma, Pc + Mc):
+        assert torch.equal(x, y)
+    # the plan entry point
+    Ps, Gs, Ms = _mixed_state(500, shapes)
+    plan = mod.MuonPlan(Ps, Gs, Ms)
+    plan.step(**HYP)
+    torch.cuda.synchronize()
+    for x, y in zip(Pa + Ma, Ps + Ms):
+        assert torch.equal(x, y)
+    plan.close()
+
+
+def test_resume_equivalence(mod):
+    """3 steps straight vs 2 steps, a host round trip of all state, 1 step."""
+    shapes = [(192, 320), (320, 192)]
+    def run(split):
+        Ps, _, Ms = _mixed_state(600, shapes, zero_mom=True)
+        for step in range(3):
+            Gs = [randn(s, 700 + 10 * step + i, 1e-3) for i, s in enumerate(shapes)]
+            mod.muon_step(Ps, Gs, Ms, **HYP)
+            if split and step == 1:
+                torch.cuda.synchronize()
+                Ps = [p.cpu().to(DEV) for p in Ps]
+                Ms = [m.cpu().to(DEV) for m in Ms]
+        torch.cuda.synchronize()
+        return Ps + Ms
+    for x, y in zip(run(False), run(True)):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------- AdamW
+
+def _adamw_close(p0, p1, Wo):
+    """fp32 AdamW against fp64: 1e-5 relative on the update, plus the fp32
+    rounding of the stored weight (one ulp of |W|)."""
+    err = np.abs(p1 - Wo)
+    tol = 1e-5 * np.abs(p0 - Wo) + np.abs(Wo) * 2.0 ** -23 + 1e-30
+    assert np.all(err <= tol), float(np.max(err / tol))
+
+
+@pytest.mark.parametrize("grad_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("t", [1, 5])
+def test_adamw(mod, grad_dtype, t):
+    sizes = [1, 3, 1536, 2049, 4096 * 3 + 5, 65536]
+    Ps = [randn((n,), 800 + i, 0.02) for i, n in enumerate(sizes)]
+    Gs = [randn((n,), 900 + i, 1e-3, grad_dtype) for i, n in enumerate(sizes)]
+    ms = [randn((n,), 1000 + i, 1e-4) if t > 1 else torch.zeros(n, device=DEV)
+          for i, n in enumerate(sizes)]
+    vs = [randn((n,), 1100 + i, 1e-4).square() if t > 1 else torch.zeros(n, device=DEV)
+          for i, n in enumerate(sizes)]
+    before = [(f64(p), f64(g), f64(m), f64(v)) for p, g, m, v in zip(Ps, Gs, ms, vs)]
+    mod.adamw_step(Ps, Gs, ms, vs, lr=1e-3, wd=0.1, step=t)
+    torch.cuda.synchronize()
+    for (p0, g0, m0, v0), p1, m1, v1 in zip(before, Ps, ms, vs):
+        Wo, mo_, vo = mo.adamw_step(p0, g0, m0, v0, lr=1e-3, wd=0.1, t=t)
+        _adamw_close(p0, f64(p1), Wo)
+        assert sp.rel_fro(f64(m1), mo_) <= 1e-6
+        assert sp.rel_fro(f64(v1), vo) <= 1e-6
+
+
+def test_optimizer_front(mod):
+    """MuonAdamW routes matrices to Muon and the rest to AdamW."""
+    mats = [torch.nn.Parameter(randn((96, 160), 1200 + i, 0.02)) for i in range(3)]
+    vecs = [torch.nn.Parameter(torch.ones(96, device=DEV))]
+    for p in mats + vecs:
+        p.grad = torch.randn_like(p) * 1e-3
+    before = [f64(p) for p in mats + vecs]
+    grads = [f64(p.grad) for p in mats + vecs]
+    opt = mod.MuonAdamW(mats, vecs, lr=1e-3, wd=0.1)
+    opt.step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        Wo, _, _, _ = mo.muon_step(before[i], grads[i], np.zeros_like(before[i]),
+                                   abc=mo.NS_COEFFS, **HYP)
+        assert sp.rel_fro(before[i] - f64(mats[i]), before[i] - Wo) <= 2e-2
+    z = np.zeros_like(before[3])
+    Wo, _, _ = mo.adamw_step(before[3], grads[3], z, z, lr=1e-3, wd=0.1, t=1)
+    _adamw_close(before[3], f64(vecs[0]), Wo)
