@@ -159,10 +159,12 @@ int mo_muon_plan_destroy(mo_muon_plan* plan);
  *                   (sqrt(v / (1 - beta2^step)) + eps)  + wd * W_old ).
  * param, state0 (m) and state1 (v) are fp32; grad is grad_dtype.  Each
  * tensor is rows * cols elements.  step >= 1 is the 1-based step count
- * used for bias correction.  Decay applies to every tensor (the pages keep
+ * used for bias correction.  beta1 and beta2 are doubles so that 1 - beta
+ * is formed exactly (0.999 rounded to fp32 would shift 1 - beta2 by
+ * 1.3e-5 relative); the elementwise arithmetic is fp32.  Decay applies to every tensor (the pages keep
  * it on RMSNorm gains too).  Needs no workspace. */
 int mo_adamw_step(const mo_tensor* tensors, int64_t count, int grad_dtype,
-                  float lr, float wd, float beta1, float beta2, float eps,
+                  float lr, float wd, double beta1, double beta2, float eps,
                   int64_t step, void* stream);
 
 /* Workspace for mo_newton_schulz on `batch` matrices [rows, cols]. */

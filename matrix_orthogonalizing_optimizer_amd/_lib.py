@@ -57,7 +57,7 @@ _SIGS = {
                                      _P, _P, _c.c_size_t, _P]),
     "mo_muon_plan_destroy": (_c.c_int, [_P]),
     "mo_adamw_step": (_c.c_int, [_c.POINTER(MoTensor), _c.c_int64, _c.c_int, _c.c_float,
-                                 _c.c_float, _c.c_float, _c.c_float, _c.c_float, _c.c_int64, _P]),
+                                 _c.c_float, _c.c_double, _c.c_double, _c.c_float, _c.c_int64, _P]),
     "mo_newton_schulz_workspace_size": (_c.c_int, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                                    _c.POINTER(_c.c_size_t)]),
     "mo_newton_schulz": (_c.c_int, [_P, _P, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,

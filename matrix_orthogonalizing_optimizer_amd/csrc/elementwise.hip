@@ -16,6 +16,7 @@
 //           parameters (section 2.2).
 // Reductions are deterministic: fixed-shape trees, no float atomics.
 #include "mo_internal.h"
+#include "mo_layout.h"
 
 namespace mo {
 
@@ -111,8 +112,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   const int esz = p.ns_dt == F32 ? 4 : 2;
   char* xrow = static_cast<char*>(p.x_row) + b * p.x_stride * esz;
   char* xt = static_cast<char*>(p.x_t) + b * p.x_stride * esz;
-  void* xnat = md.oriented ? xt : xrow;     // [A_pad, B_pad]
-  void* xtr = md.oriented ? xrow : xt;      // [B_pad, A_pad]
+  void* xnat = md.oriented ? xt : xrow;     // blocked [A_pad, B_pad]
+  void* xtr = md.oriented ? xrow : xt;      // blocked [B_pad, A_pad]
+  const Blocked Lnat = blocked(p.tile, B_pad, esz), Ltr = blocked(p.tile, A_pad, esz);
   const bool vec_ok = (B & 3) == 0;
   float sq = 0.0f;
 
@@ -147,8 +149,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
         sq += n4[j] * n4[j];
       }
     }
-    // natural layout (padding written as zeros)
-    store4(xnat, p.ns_dt, static_cast<int64_t>(r) * B_pad + c, 4, true, n4);
+    // natural layout (padding written as zeros); 4 consecutive columns
+    // stay inside one 16-byte chunk of the blocked layout
+    store4(xnat, p.ns_dt, blk_off(Lnat, r, c), 4, true, n4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) tile[rl][tx * 4 + j] = n4[j];
   }
@@ -160,8 +163,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = tile[tx * 4 + j][cl];
-    const int64_t off = static_cast<int64_t>(tb * 64 + cl) * A_pad + ta * 64 + tx * 4;
-    store4(xtr, p.ns_dt, off, 4, true, v);
+    store4(xtr, p.ns_dt, blk_off(Ltr, tb * 64 + cl, ta * 64 + tx * 4), 4, true, v);
   }
   const float s = block_sum_256(sq, red);
   if (threadIdx.x == 0) p.norm_part[static_cast<int64_t>(b) * p.tiles_per_mat + t] = s;
@@ -192,6 +194,7 @@ __global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
   const int esz = p.ns_dt == F32 ? 4 : 2;
   // the natural-layout copy of N
   const char* base = static_cast<const char*>(md.oriented ? p.x_t : p.x_row) + b * p.x_stride * esz;
+  const Blocked Lnat = blocked(p.tile, B_pad, esz);
   const float r0 = p.rscale[b];
   const float lrwd = p.lrwd;
   const int c = tb * 64 + tx * 4;
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
     const int r = ta * 64 + ty + pass * 16;
     if (r >= A || nvalid == 0) continue;
     float x[4];
-    load4(base, p.ns_dt, static_cast<int64_t>(r) * B_pad + c, 4, true, x);
+    load4(base, p.ns_dt, blk_off(Lnat, r, c), 4, true, x);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[j] = j < nvalid ? r0 * x[j] : 0.0f;

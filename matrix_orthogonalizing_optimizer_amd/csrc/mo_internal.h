@@ -26,9 +26,10 @@ static_assert(sizeof(MatDesc) == 32, "descriptor layout");
 // matrix; each tile writes the Newton-Schulz input in both layouts.
 struct PrepArgs {
   const MatDesc* desc;   // chunk's descriptors (chunk-local index)
-  void* x_row;           // [chunk][m_pad][n_pad]  (ns dtype)
-  void* x_t;             // [chunk][n_pad][m_pad]
+  void* x_row;           // [chunk] blocked [m_pad, n_pad]  (ns dtype)
+  void* x_t;             // [chunk] blocked [n_pad, m_pad]
   int64_t x_stride;      // m_pad * n_pad
+  int tile;              // panel height of the blocked layout
   int m, n, m_pad, n_pad;
   int tiles_per_mat;     // (m_pad / 64) * (n_pad / 64)
   float mu;
@@ -47,24 +48,28 @@ struct NormArgs {
 };
 
 // Epilogue kinds of the Newton-Schulz GEMM C = A * B^T.
+// The linear term a X of Eq. 2 is folded into the polynomial matrix,
+// P' = a I + b S + c S S, so the update is the plain product X' = P' X.
 enum Epi : int {
   EPI_GRAM = 0,     // C = s^2 acc, lower tiles mirrored
-  EPI_POLY = 1,     // C = c acc + b D, lower tiles mirrored
-  EPI_UPDATE = 2,   // C = s (acc + a D), also stored transposed in Ct
-  EPI_APPLY = 3,    // x = s (acc + a D); W -= lrwd W + step x (natural layout)
-  EPI_STORE = 4     // x = s (acc + a D); out = x (natural layout, ns dtype)
+  EPI_POLY = 1,     // C = alpha acc + beta D + gamma I, lower tiles mirrored
+  EPI_UPDATE = 2,   // C = s acc, also stored transposed in Ct
+  EPI_APPLY = 3,    // x = s acc; W -= lrwd W + step x (natural layout)
+  EPI_STORE = 4     // x = s acc; out = x (natural layout, ns dtype)
 };
 
+// All matrices are in the blocked layout (mo_layout.h) with panels of
+// TILE rows; s* are per-batch-entry strides in elements.
 struct GemmArgs {
-  const void* A;  int64_t sA; int lda;   // [M, K] per batch entry
-  const void* B;  int64_t sB; int ldb;   // [N, K]
-  const void* D;  int64_t sD; int ldd;   // [M, N] epilogue operand
-  void* C;        int64_t sC; int ldc;   // [M, N] output
-  void* Ct;       int64_t sCt; int ldct; // [N, M] transposed output
+  const void* A;  int64_t sA;            // [M, K] per batch entry
+  const void* B;  int64_t sB;            // [N, K]
+  const void* D;  int64_t sD;            // [M, N] epilogue operand
+  void* C;        int64_t sC;            // [M, N] output
+  void* Ct;       int64_t sCt;           // [N, M] transposed output
   int M, N, K;                           // padded sizes (tile multiples)
   int tiles_m, tiles_n, tiles_per_mat, batch;
   const float* rscale;                   // per batch entry, or null (s = 1)
-  float alpha, beta;                     // out = s (alpha acc + beta D)
+  float alpha, beta, gamma;              // EPI_POLY coefficients
   // EPI_APPLY / EPI_STORE
   const MatDesc* desc;                   // per batch entry
   void* out;  int64_t s_out;             // EPI_STORE output base, stride
@@ -77,9 +82,10 @@ struct GemmArgs {
 // steps in the Newton-Schulz-only entry point.
 struct ApplyX0Args {
   const MatDesc* desc;
-  const void* x_row;                     // [chunk][m_pad][n_pad]
-  const void* x_t;                       // [chunk][n_pad][m_pad]
+  const void* x_row;                     // [chunk] blocked [m_pad, n_pad]
+  const void* x_t;                       // [chunk] blocked [n_pad, m_pad]
   int64_t x_stride;                      // m_pad * n_pad
+  int tile;                              // panel height of the blocked layout
   int m, n, m_pad, n_pad;
   int tiles_per_mat;                     // 64x64 tiles of the true domain
   const float* rscale;

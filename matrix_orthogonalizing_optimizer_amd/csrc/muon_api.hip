@@ -354,6 +354,7 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
         a.x_row = xr[0];
         a.x_t = xt[0];
         a.x_stride = L.x_elems;
+        a.tile = tile_size(bin.cfg);
         a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
         a.tiles_per_mat = L.prep_tiles;
         a.mu = h.mu;
@@ -378,6 +379,7 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
         a.x_row = xr[0];
         a.x_t = xt[0];
         a.x_stride = L.x_elems;
+        a.tile = tile_size(bin.cfg);
         a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
         a.tiles_per_mat = L.x0_tiles;
         a.rscale = rscale;
@@ -402,41 +404,40 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
           const float* rs = k == 0 ? rscale : nullptr;
           {  // S = X X^T
             GemmArgs g{};
-            g.A = xrc; g.sA = L.x_elems; g.lda = bin.n_pad;
-            g.B = xrc; g.sB = L.x_elems; g.ldb = bin.n_pad;
-            g.C = S;   g.sC = L.s_elems; g.ldc = bin.m_pad;
+            g.A = xrc; g.sA = L.x_elems;
+            g.B = xrc; g.sB = L.x_elems;
+            g.C = S;   g.sC = L.s_elems;
             g.M = bin.m_pad; g.N = bin.m_pad; g.K = bin.n_pad;
             g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tm * (tm + 1) / 2; g.batch = chunk;
             g.rscale = rs; g.alpha = 1.0f; g.beta = 0.0f;
             ProfScope ps(MO_K_GRAM, s, chunk * m * m * n);
             if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_GRAM, g, s), s, "gram"))) return rc;
           }
-          {  // P = b S + c S S
+          {  // P' = a I + b S + c S S
             GemmArgs g{};
-            g.A = S; g.sA = L.s_elems; g.lda = bin.m_pad;
-            g.B = S; g.sB = L.s_elems; g.ldb = bin.m_pad;
-            g.D = S; g.sD = L.s_elems; g.ldd = bin.m_pad;
-            g.C = P; g.sC = L.s_elems; g.ldc = bin.m_pad;
+            g.A = S; g.sA = L.s_elems;
+            g.B = S; g.sB = L.s_elems;
+            g.D = S; g.sD = L.s_elems;
+            g.C = P; g.sC = L.s_elems;
             g.M = bin.m_pad; g.N = bin.m_pad; g.K = bin.m_pad;
             g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tm * (tm + 1) / 2; g.batch = chunk;
-            g.rscale = nullptr; g.alpha = h.c; g.beta = h.b;
+            g.rscale = nullptr; g.alpha = h.c; g.beta = h.b; g.gamma = h.a;
             ProfScope ps(MO_K_POLY, s, chunk * m * m * m);
             if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_POLY, g, s), s, "poly"))) return rc;
           }
-          {  // X' = a X + P X
+          {  // X' = P' X
             const bool last = (k + 1 == h.ns_steps);
             GemmArgs g{};
-            g.A = P;   g.sA = L.s_elems; g.lda = bin.m_pad;
-            g.B = xtc; g.sB = L.x_elems; g.ldb = bin.m_pad;
-            g.D = xrc; g.sD = L.x_elems; g.ldd = bin.n_pad;
+            g.A = P;   g.sA = L.s_elems;
+            g.B = xtc; g.sB = L.x_elems;
             g.M = bin.m_pad; g.N = bin.n_pad; g.K = bin.m_pad;
             g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.batch = chunk;
-            g.rscale = rs; g.alpha = 1.0f; g.beta = h.a;
+            g.rscale = rs;
             Epi epi = EPI_UPDATE;
             int cls = MO_K_UPDATE;
             if (!last) {
-              g.C = xrn; g.sC = L.x_elems; g.ldc = bin.n_pad;
-              g.Ct = xtn; g.sCt = L.x_elems; g.ldct = bin.m_pad;
+              g.C = xrn; g.sC = L.x_elems;
+              g.Ct = xtn; g.sCt = L.x_elems;
             } else {
               g.desc = desc;
               g.m_true = bin.m; g.n_true = bin.n;
@@ -642,15 +643,15 @@ int mo_muon_plan_destroy(mo_muon_plan* plan) {
   return rc;
 }
 
-int mo_adamw_step(const mo_tensor* tensors, int64_t count, int grad_dtype, float lr, float wd, float beta1,
-                  float beta2, float eps, int64_t step, void* stream) {
+int mo_adamw_step(const mo_tensor* tensors, int64_t count, int grad_dtype, float lr, float wd, double beta1,
+                  double beta2, float eps, int64_t step, void* stream) {
   int rc;
   if ((rc = validate_dtype(grad_dtype, "grad_dtype"))) return rc;
   if (count < 0) return fail(MO_EINVAL, "count must be >= 0");
   if (count > 0 && !tensors) return fail(MO_EINVAL, "tensors is NULL");
   if (!finite(lr) || !finite(wd) || !finite(eps) || eps < 0.0f)
     return fail(MO_EINVAL, "lr, wd must be finite; eps finite and >= 0");
-  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
     return fail(MO_EINVAL, "beta1 and beta2 must be in [0, 1)");
   if (step < 1) return fail(MO_EINVAL, "step must be >= 1");
   std::vector<Range> ranges;
@@ -674,11 +675,13 @@ int mo_adamw_step(const mo_tensor* tensors, int64_t count, int grad_dtype, float
   hipStream_t s = static_cast<hipStream_t>(stream);
   AdamArgs a{};
   a.grad_dt = grad_dtype;
-  a.lr = lr; a.wd = wd; a.beta1 = beta1; a.beta2 = beta2; a.eps = eps;
-  a.one_m_beta1 = static_cast<float>(1.0 - static_cast<double>(beta1));
-  a.one_m_beta2 = static_cast<float>(1.0 - static_cast<double>(beta2));
-  a.bc1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
-  a.bc2_rsqrt = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
+  a.lr = lr; a.wd = wd; a.eps = eps;
+  a.beta1 = static_cast<float>(beta1);
+  a.beta2 = static_cast<float>(beta2);
+  a.one_m_beta1 = static_cast<float>(1.0 - beta1);
+  a.one_m_beta2 = static_cast<float>(1.0 - beta2);
+  a.bc1 = static_cast<float>(1.0 / (1.0 - std::pow(beta1, static_cast<double>(step))));
+  a.bc2_rsqrt = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(beta2, static_cast<double>(step))));
   for (int64_t i0 = 0; i0 < count; i0 += kAdamMaxTensors) {
     const int nt = static_cast<int>(std::min<int64_t>(kAdamMaxTensors, count - i0));
     int64_t blocks = 0;

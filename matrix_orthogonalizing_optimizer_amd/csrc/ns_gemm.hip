@@ -3,9 +3,11 @@
 // Eq. 2 of "Muon is Scalable for LLM Training" (section 2.1) is evaluated as
 // three products per iteration, all of the form C = A * B^T with both
 // operands K-contiguous (row-major [rows, K]):
-//   Gram    S = X X^T          A = B = X (row-major [m, n])      symmetric
-//   Poly    P = b S + c S S^T  A = B = S (S is exactly symmetric) symmetric
-//   Update  X' = a X + P X     A = P, B = X^T (row-major [n, m])
+//   Gram    S = X X^T                  A = B = X ([m, n])             symmetric
+//   Poly    P' = a I + b S + c S S^T   A = B = S (exactly symmetric)  symmetric
+//   Update  X' = P' X                  A = P', B = X^T ([n, m])
+// (a X + b S X + c S^2 X = (a I + b S + c S^2) X: the linear term rides in
+// P', whose diagonal is near 1 on converged directions.)
 // Keeping every iterate in both layouts (the Update epilogue writes X' and
 // X'^T) makes all three the same NT kernel.  The symmetric products compute
 // only lower-triangle tiles and write each tile twice (itself and its
@@ -20,9 +22,16 @@
 // All sizes are padded by the host to tile multiples (the padding is zero
 // and stays zero through the iteration), so the main loop has no bounds
 // checks; only the apply/store epilogues check against the true sizes.
+//
+// Operands live in the blocked layout of mo_layout.h: one K-stage of one
+// row panel is a contiguous block that direct-to-LDS loads copy verbatim,
+// and an output tile is a contiguous range, so the Gram, polynomial and
+// update epilogues assemble the tile (and its mirror or transpose) in LDS
+// and stream it out with coalesced 16-byte stores.
 #include <utility>
 
 #include "mo_internal.h"
+#include "mo_layout.h"
 
 namespace mo {
 
@@ -47,6 +56,15 @@ template <> struct Elem<uint16_t> {          // bf16 storage
   static constexpr int kVec = 8;             // elements per 16-byte chunk
   __device__ static float ld(const uint16_t* p) { return bf2f(*p); }
   __device__ static void st(uint16_t* p, float v) { *p = f2bf(v); }
+  __device__ static float cvt(uint16_t h) { return bf2f(h); }
+  __device__ static uint16_t pack(float v) { return f2bf(v); }
+  // four consecutive elements (8-byte aligned) in one store
+  __device__ static void store4(uint16_t* p, float a, float b, float c, float d) {
+    uint2 q;
+    q.x = static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
+    q.y = static_cast<uint32_t>(f2bf(c)) | (static_cast<uint32_t>(f2bf(d)) << 16);
+    *reinterpret_cast<uint2*>(p) = q;
+  }
   __device__ static f32x16_t mma(u32x4 a, u32x4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -56,6 +74,11 @@ template <> struct Elem<float> {
   static constexpr int kVec = 4;
   __device__ static float ld(const float* p) { return *p; }
   __device__ static void st(float* p, float v) { *p = v; }
+  __device__ static float cvt(float v) { return v; }
+  __device__ static float pack(float v) { return v; }
+  __device__ static void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
   // The four fp32 of a lane's chunk feed four K=2 MFMAs; A and B use the
   // same component order, so the contraction covers all 8 K values.
   __device__ static f32x16_t mma(u32x4 a, u32x4 b, f32x16_t c) {
@@ -76,7 +99,47 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-constexpr int kGroupM = 8;   // tile rows per swizzle group (non-symmetric)
+constexpr int kGroupM = 8;   // tile rows per group of the tile order
+
+// Tile order of a full tiles_m x tiles_n grid: groups of kGroupM tile rows,
+// column-major inside a group, so that consecutive tiles (which run at the
+// same time on one XCD) share few A and B panels.
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, int& ti, int& tj) {
+  const int per_group = kGroupM * tiles_n;
+  const int g = t / per_group;
+  const int first = g * kGroupM;
+  const int gm = min(tiles_m - first, kGroupM);
+  const int w = t - g * per_group;
+  ti = first + w % gm;
+  tj = w / gm;
+}
+
+// The same order restricted to the lower triangle (tj <= ti) of a square
+// grid: a group of rows [r0, r0 + gm) first runs its full columns
+// tj < r0 column-major, then its own triangle.
+__device__ __forceinline__ void sym_tile(int t, int tiles_m, int& ti, int& tj) {
+  int r0 = 0, gm = 0;
+  for (;;) {
+    gm = min(tiles_m - r0, kGroupM);
+    const int n = gm * r0 + gm * (gm + 1) / 2;
+    if (t < n) break;
+    t -= n;
+    r0 += gm;
+  }
+  if (t < gm * r0) {
+    ti = r0 + t % gm;
+    tj = t / gm;
+    return;
+  }
+  t -= gm * r0;
+  int c = 0;
+  while (t >= gm - c) {
+    t -= gm - c;
+    ++c;
+  }
+  tj = r0 + c;
+  ti = r0 + c + t;
+}
 
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): the
 // indices are constants from the start, so small per-thread arrays indexed
@@ -90,66 +153,63 @@ __device__ __forceinline__ void unroll(F&& f) {
   unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most `vm`
+// vector-memory loads of this wave are outstanding; LDS and export
+// counters are left unconstrained.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | (((vm >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
+
+#define MO_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+
 template <typename T, int TILE, int EPI>
 __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   using E = Elem<T>;
   constexpr bool kSym = (EPI == EPI_GRAM || EPI == EPI_POLY);
-  constexpr int BK = 128 / sizeof(T);        // K elements per K-step
-  constexpr int WT = TILE / 2;               // wave tile edge
-  constexpr int FM = WT / 32;                // 32x32 blocks per wave edge
-  constexpr int CH = TILE * 8 / 256;         // 16-byte chunks per thread per operand
-  __shared__ u32x4 smem[2][2 * TILE * 8];
+  constexpr int kRowBytes = 64;                   // bytes of a tile row per stage
+  constexpr int BK = kRowBytes / sizeof(T);       // K elements per stage
+  constexpr int CPR = kRowBytes / 16;             // 16-byte chunks per row (4)
+  constexpr int NST = 4;                          // LDS stages (3 in flight)
+  constexpr int WT = TILE / 2;                    // wave tile edge
+  constexpr int FM = WT / 32;                     // 32x32 blocks per wave edge
+  constexpr int OPS = TILE * CPR;                 // chunks of one operand per stage
+  constexpr int STAGE = 2 * OPS;                  // chunks per stage (A then B)
+  constexpr int RPI = 64 / CPR;                   // rows per wave-wide load (16)
+  constexpr int INST = TILE / RPI / 4;            // loads per wave per operand per stage
+  constexpr int DPW = 2 * INST;                   // loads per wave per stage
+  __shared__ u32x4 smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int b = lid / p.tiles_per_mat;
   const int t = lid - b * p.tiles_per_mat;
   int ti, tj;
-  if (kSym) {
-    // lower-triangle enumeration: t = ti (ti + 1) / 2 + tj, tj <= ti
-    int r = static_cast<int>((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while (r * (r + 1) / 2 > t) --r;
-    while ((r + 1) * (r + 2) / 2 <= t) ++r;
-    ti = r;
-    tj = t - r * (r + 1) / 2;
-  } else {
-    const int per_group = kGroupM * p.tiles_n;
-    const int g = t / per_group;
-    const int first = g * kGroupM;
-    const int gm = min(p.tiles_m - first, kGroupM);
-    const int w = t - g * per_group;
-    ti = first + w % gm;
-    tj = w / gm;
-  }
+  if (kSym) sym_tile(t, p.tiles_m, ti, tj);
+  else grouped_tile(t, p.tiles_m, p.tiles_n, ti, tj);
 
-  const T* __restrict__ Ag = static_cast<const T*>(p.A) + b * p.sA + static_cast<int64_t>(ti) * TILE * p.lda;
-  const T* __restrict__ Bg = static_cast<const T*>(p.B) + b * p.sB + static_cast<int64_t>(tj) * TILE * p.ldb;
-
-  // Global -> register staging, one K-step ahead.  Thread tid moves the
-  // 16-byte chunks tid + 256 i (row = chunk / 8, column chunk = chunk % 8);
-  // rows advance by 32 per i, so the per-i offsets are constants.
-  u32x4 ra[CH], rb[CH];
-  const int srow = tid >> 3, sch = tid & 7;
-  const T* __restrict__ Ab = Ag + srow * p.lda + sch * E::kVec;
-  const T* __restrict__ Bb = Bg + srow * p.ldb + sch * E::kVec;
-  const int lda32 = 32 * p.lda, ldb32 = 32 * p.ldb;
-  const int soff0 = srow * 8 + (sch ^ (srow & 7));   // (srow + 32 i) & 7 == srow & 7
-  auto gload = [&](int k0) {
-    unroll<CH>([&](auto i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(Ab + i * lda32 + k0);
-      rb[i] = *reinterpret_cast<const u32x4*>(Bb + i * ldb32 + k0);
-    });
-  };
-  auto sstore = [&](int buf) {
-    unroll<CH>([&](auto i) {
-      smem[buf][soff0 + i * 256] = ra[i];
-      smem[buf][TILE * 8 + soff0 + i * 256] = rb[i];
-    });
-  };
+  // row panels ti of A and tj of B: nk stages of TILE x BK each
+  const int nk = p.K / BK;
+  const int64_t stage_elems = static_cast<int64_t>(TILE) * BK;
+  const T* __restrict__ Ag = static_cast<const T*>(p.A) + b * p.sA + static_cast<int64_t>(ti) * nk * stage_elems;
+  const T* __restrict__ Bg = static_cast<const T*>(p.B) + b * p.sB + static_cast<int64_t>(tj) * nk * stage_elems;
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = (wave >> 1) * WT, wc = (wave & 1) * WT;
   const int l32 = lane & 31, lh = lane >> 5;
+
+  // Direct-to-LDS loads.  A stage of a panel is one contiguous block that
+  // is already in the LDS order (64-byte rows, permuted chunks); a
+  // wave-wide global_load_lds_dwordx4 copies 1 KiB of it (lane l moves the
+  // 16 bytes at +16 l), and this wave's loads i cover 1 KiB pieces
+  // wave*INST + i of the operand's block.
+  const int goff = (wave * INST) * 64 * E::kVec + lane * E::kVec;
+  auto dma = [&](int buf, int kt) {
+    u32x4* st = smem + buf * STAGE;
+    const int64_t so = static_cast<int64_t>(kt) * stage_elems + goff;
+    unroll<INST>([&](auto i) {
+      __builtin_amdgcn_global_load_lds(Ag + so + i * 64 * E::kVec, MO_LDS(st + (wave * INST + i) * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Bg + so + i * 64 * E::kVec, MO_LDS(st + OPS + (wave * INST + i) * 64), 16, 0, 0);
+    });
+  };
 
   f32x16_t acc[FM][FM];
 #pragma unroll
@@ -159,36 +219,81 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // MFMA work of one K-step from LDS buffer `buf`.
-  auto compute = [&](int buf) {
-    const u32x4* sA = smem[buf];
-    const u32x4* sB = smem[buf] + TILE * 8;
-    unroll<4>([&](auto ks) {
-      const int chunk = (ks * 2 + lh) ^ (l32 & 7);
-      u32x4 fa[FM], fb[FM];
-      unroll<FM>([&](auto f) {
-        fa[f] = sA[(wr + f * 32 + l32) * 8 + chunk];
-        fb[f] = sB[(wc + f * 32 + l32) * 8 + chunk];
-      });
-      unroll<FM>([&](auto i) {
-        unroll<FM>([&](auto j) { acc[i][j] = E::mma(fa[i], fb[j], acc[i][j]); });
-      });
+  // A stage is two substeps of two 16-byte chunks per row.  Fragments of a
+  // substep are read from LDS (set 0 / set 1 registers) while the MFMAs of
+  // the other substep run.
+  const int rsw = (l32 >> 2) & 3;               // slot swizzle of the rows this lane reads
+  u32x4 fa[2][FM], fb[2][FM];
+  auto frags = [&](int buf, auto ks, auto set) {
+    const u32x4* sA = smem + buf * STAGE;
+    const u32x4* sB = sA + OPS;
+    const int slot = (ks * 2 + lh) ^ rsw;
+    unroll<FM>([&](auto f) {
+      fa[set][f] = sA[(wr + f * 32 + l32) * CPR + slot];
+      fb[set][f] = sB[(wc + f * 32 + l32) * CPR + slot];
     });
   };
+  auto mmas = [&](auto set) {
+    unroll<FM>([&](auto i) {
+      unroll<FM>([&](auto j) { acc[i][j] = E::mma(fa[set][i], fb[set][j], acc[i][j]); });
+    });
+  };
+  // interleave: one MFMA, one LDS read, ... then the remaining MFMAs
+  constexpr int kMfma = FM * FM * (sizeof(T) == 4 ? 4 : 1);   // MFMAs per substep
+  constexpr int kReads = 2 * FM;                              // LDS reads per substep
+  auto interleave = [&]() {
+    unroll<kReads>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+  };
+  auto wait_vm = [&](int later) {               // at most `later` stages outstanding
+    if (later >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DPW));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DPW));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(DPW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  };
+  auto barrier = [&]() {                        // no memory fence: it would drain the loads
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
-  // Double-buffered main loop; the last K-step is peeled so that the loop
-  // body has no branches and the staging registers stay in registers.
-  const int nk = p.K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    gload((kt + 1) * BK);
-    compute(kt & 1);
-    sstore((kt + 1) & 1);
-    __syncthreads();
+  // Main loop.  Stage kt lives in LDS buffer kt % NST.  Before the barrier
+  // in the middle of iteration kt a wave waits until stage kt+1 of its own
+  // loads has landed (only later stages outstanding) and its own LDS reads
+  // are done; after the barrier every wave's part of stage kt+1 is visible
+  // and buffer kt % NST (fully read) is refilled with stage kt+NST.  The
+  // barrier carries no memory fence: a fence would wait for every
+  // outstanding load and drain the pipeline.
+  const int pro = nk < NST ? nk : NST;
+  for (int s = 0; s < pro; ++s) dma(s, s);
+  wait_vm(pro - 1);
+  barrier();
+  frags(0, S0{}, S0{});
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt % NST;
+    frags(cur, S1{}, S1{});
+    mmas(S0{});
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      wait_vm(min(2, nk - 2 - kt));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      frags((kt + 1) % NST, S0{}, S0{});
+      if (kt + NST < nk) dma(cur, kt + NST);
+    }
+    mmas(S1{});
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
-  compute((nk - 1) & 1);
+  // every wave is done with the staged tiles before LDS is reused
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  barrier();
 
   // ---------------------------------------------------------------- epilogue
   // 32x32 accumulator layout: lane (l32, lh), register r holds
@@ -199,51 +304,102 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     if (EPI == EPI_GRAM) s = s * s;
   }
   const int row0 = ti * TILE + wr, col0 = tj * TILE + wc;
+  const Blocked Lc = blocked(TILE, p.N, sizeof(T));       // C and D: [M, N]
   T* __restrict__ C = static_cast<T*>(p.C) + b * p.sC;
   const T* __restrict__ D = static_cast<const T*>(p.D) + (p.D ? b * p.sD : 0);
-  constexpr bool kUsesD = (EPI != EPI_GRAM);
 
-  // Visit every accumulator element with compile-time register indices.
-  // For each 32x32 block the 16 epilogue operands D[gi][gj] are loaded
-  // first, so their loads are in flight together.
+  // Tile-local position (rr, cc) inside an LDS copy of one output tile,
+  // which has the blocked layout of the tile's contiguous global range:
+  // TILE / BK stages of TILE rows x BK elements, chunks permuted per row.
+  auto loff = [&](int rr, int cc) {
+    const int st = cc / BK, c2 = cc - st * BK, ch = c2 / E::kVec;
+    return (st * TILE + rr) * BK + ((ch ^ ((rr >> 2) & 3)) * E::kVec) + (c2 - ch * E::kVec);
+  };
+  // Visit every accumulator element with compile-time register indices,
+  // passing tile-local coordinates; the visitor returns the element's new
+  // value.
   auto for_each_acc = [&](auto&& fn) {
     unroll<FM>([&](auto i) {
       unroll<FM>([&](auto j) {
-        float dv[16];
-        const int gj = col0 + j * 32 + l32;
         unroll<16>([&](auto rc) {
           constexpr int r = decltype(rc)::value;
-          const int gi = row0 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          dv[r] = kUsesD ? E::ld(D + static_cast<int64_t>(gi) * p.ldd + gj) : 0.0f;
-        });
-        unroll<16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const int gi = row0 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          fn(gi, gj, acc[i][j][r], dv[r]);
+          const int rr = wr + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int cc = wc + j * 32 + l32;
+          acc[i][j][r] = fn(rr, cc, acc[i][j][r]);
         });
       });
     });
   };
+  T* const lt = reinterpret_cast<T*>(smem);                // TILE * TILE elements fit
+  constexpr int kTileChunks = TILE * TILE * static_cast<int>(sizeof(T)) / 16;
+  // LDS tile -> contiguous global range, 16 bytes per thread and step
+  auto copy_out = [&](T* dst) {
+    u32x4* g = reinterpret_cast<u32x4*>(dst);
+    for (int c = tid; c < kTileChunks; c += 256) g[c] = smem[c];
+  };
 
-  if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
-    const bool diag = (ti == tj);
-    for_each_acc([&](int gi, int gj, float v, float d) {
-      if (diag && gi < gj) return;
-      if (EPI == EPI_GRAM) v = s * v;
-      else v = p.alpha * v + p.beta * d;
-      E::st(C + static_cast<int64_t>(gi) * p.ldc + gj, v);
-      if (gi != gj) E::st(C + static_cast<int64_t>(gj) * p.ldc + gi, v);
+  if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY || EPI == EPI_UPDATE) {
+    if constexpr (EPI == EPI_POLY) {
+      // the operand tile S[ti, tj] (same blocked layout as C) into LDS
+      const u32x4* dsrc = reinterpret_cast<const u32x4*>(D + blk_tile(Lc, ti, tj));
+      for (int c = tid; c < kTileChunks; c += 256) {
+        const int wave_base = c - lane;                  // uniform across the wave
+        __builtin_amdgcn_global_load_lds(dsrc + c, MO_LDS(smem + wave_base), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      barrier();
+    }
+    const bool diag = kSym && (ti == tj);
+    // finished values: back into the accumulators (for the transposed pass)
+    // and into LDS at their own position; on diagonal tiles only the lower
+    // triangle is kept, written to both positions, so S and P' stay
+    // exactly symmetric
+    for_each_acc([&](int rr, int cc, float a) {
+      float v;
+      if constexpr (EPI == EPI_POLY)
+        v = p.alpha * a + p.beta * E::cvt(lt[loff(rr, cc)]) + (diag && rr == cc ? p.gamma : 0.0f);
+      else if constexpr (EPI == EPI_GRAM)
+        v = s * a;
+      else
+        v = s * a;
+      if (!(diag && rr < cc)) {
+        lt[loff(rr, cc)] = E::pack(v);
+        if (diag && rr != cc) lt[loff(cc, rr)] = E::pack(v);
+      }
+      return v;
     });
-  } else if constexpr (EPI == EPI_UPDATE) {
-    T* __restrict__ Ct = static_cast<T*>(p.Ct) + b * p.sCt;
-    for_each_acc([&](int gi, int gj, float a, float d) {
-      const float v = s * (p.alpha * a + p.beta * d);
-      E::st(C + static_cast<int64_t>(gi) * p.ldc + gj, v);
-      E::st(Ct + static_cast<int64_t>(gj) * p.ldct + gi, v);
-    });
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    copy_out(C + blk_tile(Lc, ti, tj));
+    if (!diag) {
+      // the mirror tile (symmetric products) or the transposed copy
+      // (update): four consecutive rows of a lane are four consecutive
+      // columns of the transposed tile, written as one LDS store
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      unroll<FM>([&](auto i) {
+        unroll<FM>([&](auto j) {
+          unroll<4>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int rr0 = wr + i * 32 + 8 * q + 4 * lh;
+            const int cc = wc + j * 32 + l32;
+            E::store4(lt + loff(cc, rr0), acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          });
+        });
+      });
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      if constexpr (EPI == EPI_UPDATE) {
+        const Blocked Lt = blocked(TILE, p.M, sizeof(T));  // Ct: [N, M]
+        copy_out(static_cast<T*>(p.Ct) + b * p.sCt + blk_tile(Lt, tj, ti));
+      } else {
+        copy_out(C + blk_tile(Lc, tj, ti));
+      }
+    }
   } else {
-    // EPI_APPLY / EPI_STORE: x = s (acc + a X); write at the parameter's
-    // natural position (transposed back when the matrix was oriented).
+    // EPI_APPLY / EPI_STORE: x = s acc; write at the parameter's natural
+    // position (transposed back when the matrix was oriented).
     const MatDesc md = p.desc[b];
     const int64_t ldw = md.oriented ? p.m_true : p.n_true;
     const float lrwd = p.lrwd;
@@ -253,22 +409,21 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     unroll<FM>([&](auto i) {
       unroll<FM>([&](auto j) {
         const int gj = col0 + j * 32 + l32;
-        float dv[16], wv[16];
+        float wv[16];
         int64_t off[16];
         bool ok[16];
-        // all loads of the block first (operand X and, for apply, W)
+        // all loads of the block first (for apply: W)
         unroll<16>([&](auto rc) {
           constexpr int r = decltype(rc)::value;
           const int gi = row0 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
           ok[r] = gi < p.m_true && gj < p.n_true;
           off[r] = md.oriented ? static_cast<int64_t>(gj) * ldw + gi : static_cast<int64_t>(gi) * ldw + gj;
-          dv[r] = E::ld(D + static_cast<int64_t>(gi) * p.ldd + gj);
           wv[r] = (EPI == EPI_APPLY && ok[r]) ? W[off[r]] : 0.0f;
         });
         unroll<16>([&](auto rc) {
           constexpr int r = decltype(rc)::value;
           if (!ok[r]) return;
-          const float x = s * (p.alpha * acc[i][j][r] + p.beta * dv[r]);
+          const float x = s * acc[i][j][r];
           sq += x * x;
           if constexpr (EPI == EPI_APPLY) W[off[r]] = wv[r] - (lrwd * wv[r] + p.step * x);
           else E::st(O + off[r], x);
@@ -279,8 +434,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       // block reduction of the squared update (deterministic, no atomics)
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      __syncthreads();                      // all waves are done with the LDS tiles
-      float* red = reinterpret_cast<float*>(smem[0]);
+      float* red = reinterpret_cast<float*>(smem);
       if (lane == 0) red[wave] = sq;
       __syncthreads();
       if (tid == 0)
