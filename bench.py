@@ -37,6 +37,28 @@ HBM_PEAK_GBS = 8000.0
 HYPER = dict(lr=1e-3, wd=0.1, mu=0.95, nesterov=True, rms_scale=0.2, eps=1e-7)
 
 
+def measured_traffic(workload: str, epi: int = 2):
+    """Calibrated HBM bytes per dispatch of the update GEMM from the committed
+    rocprofv3 counter summary (profiles/hbm_traffic_<workload>.json), or None
+    when there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    n = b = 0.0
+    for name, k in rec["kernels"].items():
+        if name.startswith("mo::ns_gemm_kernel") and name.endswith(f", {epi}>"):
+            n += k["dispatches"]
+            b += k["dispatches"] * k["hbm_bytes_per_dispatch"]
+    return b / n if n else None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,7 +184,7 @@ def main():
     if upd[0]:
         ach = upd[2] / (upd[1] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                    "frac": ach / peak, "traffic": None,
+                    "frac": ach / peak, "traffic": measured_traffic(wl.key),
                     "kernel": "ns_gemm update X <- aX + PX",
                     "flops_per_launch": upd[2] / upd[0], "mean_launch_ms": upd[1] / upd[0]}
     ew_bytes = wl.n_elems * W.muon_elementwise_bytes_per_elem(wl) + \
