@@ -56,6 +56,9 @@ def build(verbose: bool = False) -> str:
                 print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    # every symbol must resolve (a kernel whose host-side stub was not
+    # emitted would otherwise only fail when the library is first loaded)
+    _run(["python3", "-c", f"import ctypes; ctypes.CDLL({tmp!r}, mode=ctypes.RTLD_LOCAL)"])
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -202,14 +202,15 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // 16 bytes at +16 l), and this wave's loads i cover 1 KiB pieces
   // wave*INST + i of the operand's block.
   const int goff = (wave * INST) * 64 * E::kVec + lane * E::kVec;
-  auto dma = [&](int buf, int kt) {
-    u32x4* st = smem + buf * STAGE;
-    const int64_t so = static_cast<int64_t>(kt) * stage_elems + goff;
-    unroll<INST>([&](auto i) {
-      __builtin_amdgcn_global_load_lds(Ag + so + i * 64 * E::kVec, MO_LDS(st + (wave * INST + i) * 64), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Bg + so + i * 64 * E::kVec, MO_LDS(st + OPS + (wave * INST + i) * 64), 16, 0, 0);
-    });
+  // load q of this wave's DPW loads of stage kt into LDS buffer buf: even q
+  // are pieces of A, odd q the matching pieces of B
+  auto dma1 = [&](int buf, int kt, auto q) {
+    constexpr int i = decltype(q)::value / 2;
+    u32x4* st = smem + buf * STAGE + (q % 2 ? OPS : 0);
+    const T* src = (q % 2 ? Bg : Ag) + static_cast<int64_t>(kt) * stage_elems + goff + i * 64 * E::kVec;
+    __builtin_amdgcn_global_load_lds(static_cast<void*>(const_cast<T*>(src)), MO_LDS(st + (wave * INST + i) * 64), 16, 0, 0);
   };
+  auto dma = [&](int buf, int kt) { unroll<DPW>([&](auto q) { dma1(buf, kt, q); }); };
 
   f32x16_t acc[FM][FM];
 #pragma unroll
@@ -224,35 +225,34 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // the other substep run.
   const int rsw = (l32 >> 2) & 3;               // slot swizzle of the rows this lane reads
   u32x4 fa[2][FM], fb[2][FM];
-  auto frags = [&](int buf, auto ks, auto set) {
+  // fragment read q of substep ks into register set `set`: even q read A
+  // fragments, odd q B fragments
+  auto frag1 = [&](int buf, auto ks, auto set, auto q) {
+    constexpr int f = decltype(q)::value / 2;
     const u32x4* sA = smem + buf * STAGE;
-    const u32x4* sB = sA + OPS;
     const int slot = (ks * 2 + lh) ^ rsw;
-    unroll<FM>([&](auto f) {
-      fa[set][f] = sA[(wr + f * 32 + l32) * CPR + slot];
-      fb[set][f] = sB[(wc + f * 32 + l32) * CPR + slot];
-    });
+    if constexpr (decltype(q)::value % 2 == 0) fa[set][f] = sA[(wr + f * 32 + l32) * CPR + slot];
+    else fb[set][f] = sA[OPS + (wc + f * 32 + l32) * CPR + slot];
   };
-  auto mmas = [&](auto set) {
-    unroll<FM>([&](auto i) {
-      unroll<FM>([&](auto j) { acc[i][j] = E::mma(fa[set][i], fb[set][j], acc[i][j]); });
+  constexpr int kGroups = FM * FM;              // MFMA groups (E::mma) per substep
+  constexpr int kReads = 2 * FM;                // fragment reads per substep
+  // The MFMAs of one substep, each followed by its share of other work:
+  // fragment reads rd(q) front-loaded (their results are needed by the
+  // next substep), loads ld(q) spread evenly.  A scheduling fence after
+  // every group keeps this order, so memory instructions never queue up
+  // in front of an MFMA.
+  auto pipelined = [&](auto set, auto nld, auto&& rd, auto&& ld) {
+    constexpr int kLd = std::decay_t<decltype(nld)>::value;
+    unroll<kGroups>([&](auto g) {
+      constexpr int G = decltype(g)::value;
+      acc[G / FM][G % FM] = E::mma(fa[set][G / FM], fb[set][G % FM], acc[G / FM][G % FM]);
+      constexpr int r0 = kReads <= kGroups ? G : G * kReads / kGroups;
+      constexpr int r1 = kReads <= kGroups ? (G < kReads ? G + 1 : G) : (G + 1) * kReads / kGroups;
+      unroll<r1 - r0>([&](auto k) { rd(std::integral_constant<int, r0 + decltype(k)::value>{}); });
+      constexpr int l0 = G * kLd / kGroups, l1 = (G + 1) * kLd / kGroups;
+      unroll<l1 - l0>([&](auto k) { ld(std::integral_constant<int, l0 + decltype(k)::value>{}); });
+      __builtin_amdgcn_sched_barrier(0);
     });
-  };
-  // interleave: one MFMA, one LDS read, ... then the remaining MFMAs
-  constexpr int kMfma = FM * FM * (sizeof(T) == 4 ? 4 : 1);   // MFMAs per substep
-  constexpr int kReads = 2 * FM;                              // LDS reads per substep
-  auto interleave = [&]() {
-    unroll<kReads>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-  };
-  auto wait_vm = [&](int later) {               // at most `later` stages outstanding
-    if (later >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DPW));
-    else if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DPW));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(DPW));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   };
   auto barrier = [&]() {                        // no memory fence: it would drain the loads
     __builtin_amdgcn_sched_barrier(0);
@@ -261,37 +261,39 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using L0 = std::integral_constant<int, 0>;
+  using LD = std::integral_constant<int, DPW>;
+  auto no_ld = [](auto) {};
 
-  // Main loop.  Stage kt lives in LDS buffer kt % NST.  Before the barrier
-  // in the middle of iteration kt a wave waits until stage kt+1 of its own
-  // loads has landed (only later stages outstanding) and its own LDS reads
-  // are done; after the barrier every wave's part of stage kt+1 is visible
-  // and buffer kt % NST (fully read) is refilled with stage kt+NST.  The
-  // barrier carries no memory fence: a fence would wait for every
-  // outstanding load and drain the pipeline.
-  const int pro = nk < NST ? nk : NST;
-  for (int s = 0; s < pro; ++s) dma(s, s);
-  wait_vm(pro - 1);
+  // Main loop.  Stage kt lives in LDS buffer kt % NST.  Every iteration
+  // issues exactly one stage of loads (stage kt + NST, or -- past the end
+  // -- the last stage again into the buffer that has just been consumed),
+  // so the number of loads in flight is the same at every barrier and the
+  // loop body has no branch.  Before the barrier a wave waits until stage
+  // kt + 1 of its own loads has landed (two later stages may still be in
+  // flight) and its own LDS reads are done; after the barrier every wave's
+  // part of stage kt + 1 is visible and buffer kt % NST (fully read) may be
+  // refilled.  The barrier carries no memory fence: a fence would wait for
+  // every outstanding load.
+  for (int s = 0; s < NST; ++s) dma(s, min(s, nk - 1));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 1) * DPW));
   barrier();
-  frags(0, S0{}, S0{});
+  unroll<kReads>([&](auto q) { frag1(0, S0{}, S0{}, q); });
+  __builtin_amdgcn_sched_barrier(0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt % NST;
-    frags(cur, S1{}, S1{});
-    mmas(S0{});
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      wait_vm(min(2, nk - 2 - kt));
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      barrier();
-      frags((kt + 1) % NST, S0{}, S0{});
-      if (kt + NST < nk) dma(cur, kt + NST);
-    }
-    mmas(S1{});
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
+    pipelined(S0{}, L0{}, [&](auto q) { frag1(cur, S1{}, S1{}, q); }, no_ld);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * DPW));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    const int nxt = (kt + 1) % NST;
+    const int kl = min(kt + NST, nk - 1);
+    pipelined(S1{}, LD{}, [&](auto q) { frag1(nxt, S0{}, S0{}, q); },
+              [&](auto q) { dma1(cur, kl, q); });
   }
-  // every wave is done with the staged tiles before LDS is reused
+  // every load has landed and every wave is done with the staged tiles
+  // before LDS is reused
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   barrier();
 
