@@ -51,19 +51,41 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32,
+// packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> {          // bf16 storage
   static constexpr int kVec = 8;             // elements per 16-byte chunk
   __device__ static float ld(const uint16_t* p) { return bf2f(*p); }
   __device__ static void st(uint16_t* p, float v) { *p = f2bf(v); }
-  __device__ static float cvt(uint16_t h) { return bf2f(h); }
-  __device__ static uint16_t pack(float v) { return f2bf(v); }
-  // four consecutive elements (8-byte aligned) in one store
+  // four consecutive elements (8-byte aligned) in one store / one load
   __device__ static void store4(uint16_t* p, float a, float b, float c, float d) {
     uint2 q;
-    q.x = static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
-    q.y = static_cast<uint32_t>(f2bf(c)) | (static_cast<uint32_t>(f2bf(d)) << 16);
+    q.x = pack_bf16x2(a, b);
+    q.y = pack_bf16x2(c, d);
     *reinterpret_cast<uint2*>(p) = q;
+  }
+  __device__ static void load4(const uint16_t* p, float (&v)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(q.x << 16);
+    v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16);
+    v[3] = __uint_as_float(q.y & 0xffff0000u);
+  }
+  __device__ static void store1(uint16_t* p, float a) { *p = static_cast<uint16_t>(pack_bf16x2(a, a)); }
+  // two elements to two unrelated places (one conversion)
+  __device__ static void store2(uint16_t* p0, uint16_t* p1, float a, float b) {
+    const uint32_t u = pack_bf16x2(a, b);
+    *p0 = static_cast<uint16_t>(u);
+    *p1 = static_cast<uint16_t>(u >> 16);
   }
   __device__ static f32x16_t mma(u32x4 a, u32x4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -74,10 +96,17 @@ template <> struct Elem<float> {
   static constexpr int kVec = 4;
   __device__ static float ld(const float* p) { return *p; }
   __device__ static void st(float* p, float v) { *p = v; }
-  __device__ static float cvt(float v) { return v; }
-  __device__ static float pack(float v) { return v; }
   __device__ static void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+  __device__ static void load4(const float* p, float (&v)[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  __device__ static void store1(float* p, float a) { *p = a; }
+  __device__ static void store2(float* p0, float* p1, float a, float b) {
+    *p0 = a;
+    *p1 = b;
   }
   // The four fp32 of a lane's chunk feed four K=2 MFMAs; A and B use the
   // same component order, so the contraction covers all 8 K values.
@@ -176,7 +205,14 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   constexpr int RPI = 64 / CPR;                   // rows per wave-wide load (16)
   constexpr int INST = TILE / RPI / 4;            // loads per wave per operand per stage
   constexpr int DPW = 2 * INST;                   // loads per wave per stage
-  __shared__ u32x4 smem[NST * STAGE];
+  // The apply/store epilogue stages the fp32 update through LDS in passes
+  // of kPR tile rows, as [kPR][TILE + 4] (parameter rows = tile rows) or
+  // [TILE][kPR + 4] (oriented parameters: parameter rows = tile columns).
+  constexpr bool kApply = (EPI == EPI_APPLY || EPI == EPI_STORE);
+  constexpr int kPR = TILE == 256 ? 128 : TILE;
+  constexpr int kApplyFloats = TILE * (kPR + 4) > kPR * (TILE + 8) ? TILE * (kPR + 4) : kPR * (TILE + 8);
+  constexpr int kSmemChunks = (kApply && kApplyFloats / 4 > NST * STAGE) ? kApplyFloats / 4 : NST * STAGE;
+  __shared__ u32x4 smem[kSmemChunks];
 
   const int tid = threadIdx.x;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -305,7 +341,6 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     s = p.rscale[b];
     if (EPI == EPI_GRAM) s = s * s;
   }
-  const int row0 = ti * TILE + wr, col0 = tj * TILE + wc;
   const Blocked Lc = blocked(TILE, p.N, sizeof(T));       // C and D: [M, N]
   T* __restrict__ C = static_cast<T*>(p.C) + b * p.sC;
   const T* __restrict__ D = static_cast<const T*>(p.D) + (p.D ? b * p.sD : 0);
@@ -317,125 +352,267 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     const int st = cc / BK, c2 = cc - st * BK, ch = c2 / E::kVec;
     return (st * TILE + rr) * BK + ((ch ^ ((rr >> 2) & 3)) * E::kVec) + (c2 - ch * E::kVec);
   };
-  // Visit every accumulator element with compile-time register indices,
-  // passing tile-local coordinates; the visitor returns the element's new
-  // value.
-  auto for_each_acc = [&](auto&& fn) {
-    unroll<FM>([&](auto i) {
-      unroll<FM>([&](auto j) {
-        unroll<16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const int rr = wr + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int cc = wc + j * 32 + l32;
-          acc[i][j][r] = fn(rr, cc, acc[i][j][r]);
-        });
-      });
-    });
-  };
   T* const lt = reinterpret_cast<T*>(smem);                // TILE * TILE elements fit
   constexpr int kTileChunks = TILE * TILE * static_cast<int>(sizeof(T)) / 16;
-  // LDS tile -> contiguous global range, 16 bytes per thread and step
+  // LDS tile -> contiguous global range: 16 bytes per thread and step, eight
+  // steps' loads in flight before their stores
   auto copy_out = [&](T* dst) {
     u32x4* g = reinterpret_cast<u32x4*>(dst);
-    for (int c = tid; c < kTileChunks; c += 256) g[c] = smem[c];
+    constexpr int kIter = kTileChunks / 256;
+    constexpr int kB = kIter < 8 ? kIter : 8;
+#pragma unroll
+    for (int c0 = 0; c0 < kIter; c0 += kB) {
+      u32x4 v[kB];
+      unroll<kB>([&](auto k) { v[decltype(k)::value] = smem[tid + (c0 + decltype(k)::value) * 256]; });
+      unroll<kB>([&](auto k) { g[tid + (c0 + decltype(k)::value) * 256] = v[decltype(k)::value]; });
+    }
   };
 
   if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY || EPI == EPI_UPDATE) {
+    // Accumulator element (i, j, r) sits at tile row wr + 32 i + 8 q + 4 lh
+    // + e (q = r / 4, e = r % 4) and column wc + 32 j + l32.  Its LDS offset
+    // is a per-lane base plus a compile-time displacement:
+    //   direct    (rr, cc): od[q % 2] + (32 i + 8 (q - q % 2) + e) BK
+    //                        + (32 j / BK) TILE BK
+    //   transposed (cc, rr): ot[q] + (32 i / BK) TILE BK + 32 j BK + e,
+    //                        the four e consecutive (one 8- or 16-byte access)
+    // (whole 32-row / 32-column steps keep the chunk permutation, which
+    // depends on bits 2-3 of the row only).
+    int od[2], ot[4];
+    unroll<2>([&](auto q) { od[q] = loff(wr + 8 * q + 4 * lh, wc + l32); });
+    unroll<4>([&](auto q) { ot[q] = loff(wc + l32, wr + 8 * q + 4 * lh); });
+    auto doff = [&](auto i, auto j, auto r) {
+      constexpr int I = decltype(i)::value, J = decltype(j)::value, R = decltype(r)::value;
+      constexpr int Q = R / 4, e = R % 4;
+      return od[Q % 2] + (32 * I + 8 * (Q - Q % 2) + e) * BK + (32 * J / BK) * TILE * BK;
+    };
+    auto toff = [&](auto i, auto j, auto q) {
+      constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+      return ot[Q] + (32 * I / BK) * TILE * BK + 32 * J * BK;
+    };
+    const bool diag = kSym && (ti == tj);
+
     if constexpr (EPI == EPI_POLY) {
-      // the operand tile S[ti, tj] (same blocked layout as C) into LDS
-      const u32x4* dsrc = reinterpret_cast<const u32x4*>(D + blk_tile(Lc, ti, tj));
+      // b S + a I from the mirror tile S[tj, ti] (S is exactly symmetric):
+      // element (rr, cc) of this tile is (cc, rr) there, so each lane reads
+      // its four consecutive rows with one access
+      const u32x4* dsrc = reinterpret_cast<const u32x4*>(D + blk_tile(Lc, tj, ti));
       for (int c = tid; c < kTileChunks; c += 256) {
         const int wave_base = c - lane;                  // uniform across the wave
-        __builtin_amdgcn_global_load_lds(dsrc + c, MO_LDS(smem + wave_base), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<void*>(const_cast<u32x4*>(dsrc + c)),
+                                         MO_LDS(smem + wave_base), 16, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       barrier();
-    }
-    const bool diag = kSym && (ti == tj);
-    // finished values: back into the accumulators (for the transposed pass)
-    // and into LDS at their own position; on diagonal tiles only the lower
-    // triangle is kept, written to both positions, so S and P' stay
-    // exactly symmetric
-    for_each_acc([&](int rr, int cc, float a) {
-      float v;
-      if constexpr (EPI == EPI_POLY)
-        v = p.alpha * a + p.beta * E::cvt(lt[loff(rr, cc)]) + (diag && rr == cc ? p.gamma : 0.0f);
-      else if constexpr (EPI == EPI_GRAM)
-        v = s * a;
-      else
-        v = s * a;
-      if (!(diag && rr < cc)) {
-        lt[loff(rr, cc)] = E::pack(v);
-        if (diag && rr != cc) lt[loff(cc, rr)] = E::pack(v);
-      }
-      return v;
-    });
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    barrier();
-    copy_out(C + blk_tile(Lc, ti, tj));
-    if (!diag) {
-      // the mirror tile (symmetric products) or the transposed copy
-      // (update): four consecutive rows of a lane are four consecutive
-      // columns of the transposed tile, written as one LDS store
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      barrier();
       unroll<FM>([&](auto i) {
         unroll<FM>([&](auto j) {
-          unroll<4>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            const int rr0 = wr + i * 32 + 8 * q + 4 * lh;
-            const int cc = wc + j * 32 + l32;
-            E::store4(lt + loff(cc, rr0), acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                      acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          unroll<4>([&](auto q) {
+            constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+            float d[4];
+            E::load4(lt + toff(i, j, q), d);
+            unroll<4>([&](auto e) {
+              constexpr int R = 4 * Q + decltype(e)::value;
+              acc[I][J][R] = p.alpha * acc[I][J][R] + p.beta * d[decltype(e)::value];
+            });
           });
         });
       });
+      if (diag && wr == wc) {
+        unroll<FM>([&](auto i) {
+          constexpr int I = decltype(i)::value;
+          unroll<16>([&](auto r) {
+            constexpr int R = decltype(r)::value;
+            if (l32 == 8 * (R / 4) + 4 * lh + (R % 4)) acc[I][I][R] += p.gamma;
+          });
+        });
+      }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      barrier();
+      barrier();                                  // the S tile is no longer needed
+    } else {
+      unroll<FM>([&](auto i) {
+        unroll<FM>([&](auto j) {
+          unroll<16>([&](auto r) {
+            acc[decltype(i)::value][decltype(j)::value][decltype(r)::value] *= s;
+          });
+        });
+      });
+    }
+
+    // transposed pass: value (rr, cc) to LDS position (cc, rr), four rows of
+    // a lane in one store.  This is the mirror tile (symmetric products) or
+    // the tile of X'^T (update); on a diagonal tile it puts every value at
+    // its mirror position and the direct pass below then overwrites the
+    // lower triangle, leaving the tile exactly symmetric.
+    unroll<FM>([&](auto i) {
+      unroll<FM>([&](auto j) {
+        unroll<4>([&](auto q) {
+          constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+          E::store4(lt + toff(i, j, q), acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
+                    acc[I][J][4 * Q + 3]);
+        });
+      });
+    });
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    if (!diag) {
       if constexpr (EPI == EPI_UPDATE) {
         const Blocked Lt = blocked(TILE, p.M, sizeof(T));  // Ct: [N, M]
         copy_out(static_cast<T*>(p.Ct) + b * p.sCt + blk_tile(Lt, tj, ti));
       } else {
         copy_out(C + blk_tile(Lc, tj, ti));
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
     }
-  } else {
-    // EPI_APPLY / EPI_STORE: x = s acc; write at the parameter's natural
-    // position (transposed back when the matrix was oriented).
-    const MatDesc md = p.desc[b];
-    const int64_t ldw = md.oriented ? p.m_true : p.n_true;
-    const float lrwd = p.lrwd;
-    float sq = 0.0f;
-    float* __restrict__ W = md.param;
-    T* __restrict__ O = EPI == EPI_STORE ? static_cast<T*>(p.out) + b * p.s_out : nullptr;
-    unroll<FM>([&](auto i) {
-      unroll<FM>([&](auto j) {
-        const int gj = col0 + j * 32 + l32;
-        float wv[16];
-        int64_t off[16];
-        bool ok[16];
-        // all loads of the block first (for apply: W)
-        unroll<16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const int gi = row0 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          ok[r] = gi < p.m_true && gj < p.n_true;
-          off[r] = md.oriented ? static_cast<int64_t>(gj) * ldw + gi : static_cast<int64_t>(gi) * ldw + gj;
-          wv[r] = (EPI == EPI_APPLY && ok[r]) ? W[off[r]] : 0.0f;
-        });
-        unroll<16>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          if (!ok[r]) return;
-          const float x = s * acc[i][j][r];
-          sq += x * x;
-          if constexpr (EPI == EPI_APPLY) W[off[r]] = wv[r] - (lrwd * wv[r] + p.step * x);
-          else E::st(O + off[r], x);
+    // direct pass: value (rr, cc) to LDS position (rr, cc); on a diagonal
+    // tile only the lower triangle rr >= cc
+    auto direct_block = [&](auto i, auto j, bool lower_only) {
+      constexpr int I = decltype(i)::value, J = decltype(j)::value;
+      unroll<8>([&](auto h) {
+        constexpr int R0 = 2 * decltype(h)::value;
+        const int o0 = doff(i, j, std::integral_constant<int, R0>{});
+        const int o1 = doff(i, j, std::integral_constant<int, R0 + 1>{});
+        if (!lower_only) {
+          E::store2(lt + o0, lt + o1, acc[I][J][R0], acc[I][J][R0 + 1]);
+        } else {
+          // rows 8 q + 4 lh + e against column l32 of the same 32x32 block
+          const int rel = 8 * (R0 / 4) + 4 * lh + (R0 % 4);
+          if (rel >= l32) E::store1(lt + o0, acc[I][J][R0]);
+          if (rel + 1 >= l32) E::store1(lt + o1, acc[I][J][R0 + 1]);
+        }
+      });
+    };
+    if (!diag) {
+      unroll<FM>([&](auto i) { unroll<FM>([&](auto j) { direct_block(i, j, false); }); });
+    } else {
+      unroll<FM>([&](auto i) {
+        unroll<FM>([&](auto j) {
+          const int br = wr + 32 * decltype(i)::value, bc = wc + 32 * decltype(j)::value;
+          if (br > bc) direct_block(i, j, false);
+          else if (br == bc) direct_block(i, j, true);
         });
       });
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    copy_out(C + blk_tile(Lc, ti, tj));
+  } else {
+    // EPI_APPLY / EPI_STORE: x = s acc, applied at the parameter's natural
+    // position (transposed back when the matrix was oriented):
+    //   W <- W - (lr wd W + lr scale x)   or   out <- x.
+    // Each pass stages kPR tile rows of x (fp32) in LDS in the parameter's
+    // orientation; then every thread handles groups of four elements that
+    // are consecutive along a parameter row: one 16-byte LDS read, one
+    // 16-byte load and store of W.
+    const MatDesc md = p.desc[b];
+    const bool ori = md.oriented != 0;
+    const int64_t ldw = ori ? p.m_true : p.n_true;         // parameter row length
+    const int wrows = ori ? p.n_true : p.m_true;            // parameter rows
+    const float lrwd = p.lrwd, stp = p.step;
+    float* __restrict__ W = md.param;
+    T* __restrict__ O = EPI == EPI_STORE ? static_cast<T*>(p.out) + b * p.s_out : nullptr;
+    float* const lf = reinterpret_cast<float*>(smem);
+    // padded LDS row lengths: the lh = 1 half-wave writes 4 rows below the
+    // lh = 0 half, 32 banks away
+    constexpr int kLd = TILE + 8, kLdT = kPR + 4;
+    const bool full = (ti + 1) * TILE <= p.m_true && (tj + 1) * TILE <= p.n_true && (ldw % 4) == 0;
+    float sq = 0.0f;
+    auto apply4 = [&](int64_t off, int wcol, const float (&x)[4]) {
+      if (full) {
+        if constexpr (EPI == EPI_APPLY) {
+          float4 w = *reinterpret_cast<const float4*>(W + off);
+          w.x = w.x - (lrwd * w.x + stp * x[0]);
+          w.y = w.y - (lrwd * w.y + stp * x[1]);
+          w.z = w.z - (lrwd * w.z + stp * x[2]);
+          w.w = w.w - (lrwd * w.w + stp * x[3]);
+          *reinterpret_cast<float4*>(W + off) = w;
+        } else {
+          E::store4(O + off, x[0], x[1], x[2], x[3]);
+        }
+        sq += (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
+      } else {
+        unroll<4>([&](auto k) {
+          constexpr int K = decltype(k)::value;
+          if (wcol + K < ldw) {
+            if constexpr (EPI == EPI_APPLY) {
+              const float w = W[off + K];
+              W[off + K] = w - (lrwd * w + stp * x[K]);
+            } else {
+              E::st(O + off + K, x[K]);
+            }
+            sq += x[K] * x[K];
+          }
+        });
+      }
+    };
+    constexpr int kNP = TILE / kPR;
+    unroll<kNP>([&](auto pc) {
+      constexpr int pass = decltype(pc)::value;
+      if (pass > 0) barrier();                              // previous pass fully read
+      if (wr / kPR == pass) {
+        const int r_base = wr - pass * kPR;
+        unroll<FM>([&](auto i) {
+          unroll<FM>([&](auto j) {
+            unroll<4>([&](auto q) {
+              constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+              const int rr = r_base + 32 * I + 8 * Q + 4 * lh;  // tile row (within the pass) of e = 0
+              const int cc = wc + 32 * J + l32;
+              const float x0 = s * acc[I][J][4 * Q], x1 = s * acc[I][J][4 * Q + 1];
+              const float x2 = s * acc[I][J][4 * Q + 2], x3 = s * acc[I][J][4 * Q + 3];
+              if (ori) {
+                *reinterpret_cast<float4*>(lf + cc * kLdT + rr) = make_float4(x0, x1, x2, x3);
+              } else {
+                lf[(rr + 0) * kLd + cc] = x0;
+                lf[(rr + 1) * kLd + cc] = x1;
+                lf[(rr + 2) * kLd + cc] = x2;
+                lf[(rr + 3) * kLd + cc] = x3;
+              }
+            });
+          });
+        });
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      constexpr int kGroups = kPR * TILE / 4;
+      static_assert(kGroups % (256 * 4) == 0 || kGroups < 256 * 4, "group loop");
+      constexpr int kU = kGroups >= 256 * 4 ? 4 : 1;
+#pragma unroll 1
+      for (int g0 = 0; g0 < kGroups; g0 += 256 * kU) {
+        float x[kU][4];
+        int64_t off[kU];
+        int wcol[kU];
+        bool rowok[kU];
+        unroll<kU>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          const int g = g0 + U * 256 + tid;
+          int lo, wrow;
+          if (ori) {              // parameter row = tile column
+            const int cc = g / (kPR / 4), r4 = (g % (kPR / 4)) * 4;
+            lo = cc * kLdT + r4;
+            wrow = tj * TILE + cc;
+            wcol[U] = ti * TILE + pass * kPR + r4;
+          } else {
+            const int r = g / (TILE / 4), c4 = (g % (TILE / 4)) * 4;
+            lo = r * kLd + c4;
+            wrow = ti * TILE + pass * kPR + r;
+            wcol[U] = tj * TILE + c4;
+          }
+          const float4 v = *reinterpret_cast<const float4*>(lf + lo);
+          x[U][0] = v.x; x[U][1] = v.y; x[U][2] = v.z; x[U][3] = v.w;
+          rowok[U] = wrow < wrows && wcol[U] < ldw;
+          off[U] = static_cast<int64_t>(wrow) * ldw + wcol[U];
+        });
+        unroll<kU>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          if (rowok[U]) apply4(off[U], wcol[U], x[U]);
+        });
+      }
     });
     if (p.rms_part) {
       // block reduction of the squared update (deterministic, no atomics)
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      barrier();                                            // LDS reads of the last pass done
       float* red = reinterpret_cast<float*>(smem);
       if (lane == 0) red[wave] = sq;
       __syncthreads();
