@@ -98,23 +98,24 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 
 // One 64x64 tile of the padded natural domain [A_pad, B_pad] per block.
 // Thread layout: 16 threads x 4 columns across a row, 16 rows per pass.
+// The Newton-Schulz input is written once, in the oriented layout
+// [m_pad, n_pad]: straight through for a wide parameter, transposed through
+// an LDS tile for a tall one (its columns are the rows of X).
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   __shared__ float tile[64][65];
   __shared__ float red[4];
   const int b = blockIdx.x / p.tiles_per_mat;
   const int t = blockIdx.x - b * p.tiles_per_mat;
   const MatDesc md = p.desc[b];
-  const int A = md.oriented ? p.n : p.m, B = md.oriented ? p.m : p.n;
-  const int A_pad = md.oriented ? p.n_pad : p.m_pad, B_pad = md.oriented ? p.m_pad : p.n_pad;
+  const bool ori = md.oriented != 0;
+  const int A = ori ? p.n : p.m, B = ori ? p.m : p.n;
+  const int B_pad = ori ? p.m_pad : p.n_pad;
   const int tiles_b = B_pad >> 6;
   const int ta = t / tiles_b, tb = t - ta * tiles_b;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int esz = p.ns_dt == F32 ? 4 : 2;
-  char* xrow = static_cast<char*>(p.x_row) + b * p.x_stride * esz;
-  char* xt = static_cast<char*>(p.x_t) + b * p.x_stride * esz;
-  void* xnat = md.oriented ? xt : xrow;     // blocked [A_pad, B_pad]
-  void* xtr = md.oriented ? xrow : xt;      // blocked [B_pad, A_pad]
-  const Blocked Lnat = blocked(p.tile, B_pad, esz), Ltr = blocked(p.tile, A_pad, esz);
+  char* x = static_cast<char*>(p.x) + b * p.x_stride * esz;
+  const Blocked Lx = blocked(p.tile, p.n_pad, esz);      // X: [m_pad, n_pad]
   const bool vec_ok = (B & 3) == 0;
   float sq = 0.0f;
 
@@ -149,21 +150,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
         sq += n4[j] * n4[j];
       }
     }
-    // natural layout (padding written as zeros); 4 consecutive columns
-    // stay inside one 16-byte chunk of the blocked layout
-    store4(xnat, p.ns_dt, blk_off(Lnat, r, c), 4, true, n4);
+    if (!ori) {
+      // padding written as zeros; 4 consecutive columns stay inside one
+      // 16-byte chunk of the blocked layout
+      store4(x, p.ns_dt, blk_off(Lx, r, c), 4, true, n4);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile[rl][tx * 4 + j] = n4[j];
+      for (int j = 0; j < 4; ++j) tile[rl][tx * 4 + j] = n4[j];
+    }
   }
-  __syncthreads();
-  // transposed layout: rows of xtr are columns of the tile
+  if (ori) {
+    __syncthreads();
+    // rows of X are columns of the tile
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int cl = ty + pass * 16;           // tile column -> xtr row
-    float v[4];
+    for (int pass = 0; pass < 4; ++pass) {
+      const int cl = ty + pass * 16;
+      float v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = tile[tx * 4 + j][cl];
-    store4(xtr, p.ns_dt, blk_off(Ltr, tb * 64 + cl, ta * 64 + tx * 4), 4, true, v);
+      for (int j = 0; j < 4; ++j) v[j] = tile[tx * 4 + j][cl];
+      store4(x, p.ns_dt, blk_off(Lx, tb * 64 + cl, ta * 64 + tx * 4), 4, true, v);
+    }
   }
   const float s = block_sum_256(sq, red);
   if (threadIdx.x == 0) p.norm_part[static_cast<int64_t>(b) * p.tiles_per_mat + t] = s;
@@ -187,14 +193,13 @@ __global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
   const int t = blockIdx.x - b * p.tiles_per_mat;
   const MatDesc md = p.desc[b];
   const int A = md.oriented ? p.n : p.m, B = md.oriented ? p.m : p.n;
-  const int B_pad = md.oriented ? p.m_pad : p.n_pad;
   const int tiles_b = (B + 63) >> 6;
   const int ta = t / tiles_b, tb = t - ta * tiles_b;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int esz = p.ns_dt == F32 ? 4 : 2;
-  // the natural-layout copy of N
-  const char* base = static_cast<const char*>(md.oriented ? p.x_t : p.x_row) + b * p.x_stride * esz;
-  const Blocked Lnat = blocked(p.tile, B_pad, esz);
+  // N in the oriented layout X [m_pad, n_pad] (transposed for a tall parameter)
+  const char* base = static_cast<const char*>(p.x) + b * p.x_stride * esz;
+  const Blocked Lx = blocked(p.tile, p.n_pad, esz);
   const float r0 = p.rscale[b];
   const float lrwd = p.lrwd;
   const int c = tb * 64 + tx * 4;
@@ -206,7 +211,16 @@ __global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
     const int r = ta * 64 + ty + pass * 16;
     if (r >= A || nvalid == 0) continue;
     float x[4];
-    load4(base, p.ns_dt, blk_off(Lnat, r, c), 4, true, x);
+    if (!md.oriented) {
+      load4(base, p.ns_dt, blk_off(Lx, r, c), 4, true, x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4];
+        load4(base, p.ns_dt, blk_off(Lx, c + j, r), 1, false, v);
+        x[j] = v[0];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[j] = j < nvalid ? r0 * x[j] : 0.0f;

@@ -26,8 +26,7 @@ static_assert(sizeof(MatDesc) == 32, "descriptor layout");
 // matrix; each tile writes the Newton-Schulz input in both layouts.
 struct PrepArgs {
   const MatDesc* desc;   // chunk's descriptors (chunk-local index)
-  void* x_row;           // [chunk] blocked [m_pad, n_pad]  (ns dtype)
-  void* x_t;             // [chunk] blocked [n_pad, m_pad]
+  void* x;               // [chunk] blocked [m_pad, n_pad]  (ns dtype), oriented
   int64_t x_stride;      // m_pad * n_pad
   int tile;              // panel height of the blocked layout
   int m, n, m_pad, n_pad;
@@ -53,19 +52,18 @@ struct NormArgs {
 enum Epi : int {
   EPI_GRAM = 0,     // C = s^2 acc, lower tiles mirrored
   EPI_POLY = 1,     // C = alpha acc + beta D + gamma I, lower tiles mirrored
-  EPI_UPDATE = 2,   // C = s acc, also stored transposed in Ct
-  EPI_APPLY = 3,    // x = s acc; W -= lrwd W + step x (natural layout)
-  EPI_STORE = 4     // x = s acc; out = x (natural layout, ns dtype)
+  EPI_UPDATE = 2,   // C = s acc (B given K-major)
+  EPI_APPLY = 3,    // x = s acc; W -= lrwd W + step x (natural layout; B K-major)
+  EPI_STORE = 4     // x = s acc; out = x (natural layout, ns dtype; B K-major)
 };
 
 // All matrices are in the blocked layout (mo_layout.h) with panels of
 // TILE rows; s* are per-batch-entry strides in elements.
 struct GemmArgs {
   const void* A;  int64_t sA;            // [M, K] per batch entry
-  const void* B;  int64_t sB;            // [N, K]
+  const void* B;  int64_t sB;            // [N, K]; [K, N] for EPI_UPDATE/APPLY/STORE
   const void* D;  int64_t sD;            // [M, N] epilogue operand
   void* C;        int64_t sC;            // [M, N] output
-  void* Ct;       int64_t sCt;           // [N, M] transposed output
   int M, N, K;                           // padded sizes (tile multiples)
   int tiles_m, tiles_n, tiles_per_mat, batch;
   const float* rscale;                   // per batch entry, or null (s = 1)
@@ -82,8 +80,7 @@ struct GemmArgs {
 // steps in the Newton-Schulz-only entry point.
 struct ApplyX0Args {
   const MatDesc* desc;
-  const void* x_row;                     // [chunk] blocked [m_pad, n_pad]
-  const void* x_t;                       // [chunk] blocked [n_pad, m_pad]
+  const void* x;                         // [chunk] blocked [m_pad, n_pad], oriented
   int64_t x_stride;                      // m_pad * n_pad
   int tile;                              // panel height of the blocked layout
   int m, n, m_pad, n_pad;

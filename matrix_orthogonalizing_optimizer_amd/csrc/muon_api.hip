@@ -253,7 +253,7 @@ int build_plan(const mo_tensor* t, int64_t count, int grad_dt, int mom_dt, int n
 // Workspace layout ---------------------------------------------------------
 // [descriptor table (one-shot calls only)] [rscale: count floats]
 // then, reused by every bin in turn, for a chunk of `cap` matrices:
-// [norm partials] [rms partials] [X row][X^T][X' row][X'^T][S][P]
+// [norm partials] [rms partials] [X][X'][S][P]
 struct BinLayout {
   int64_t x_elems, s_elems;
   int prep_tiles, upd_tiles, x0_tiles, rms_tiles;
@@ -270,7 +270,7 @@ BinLayout bin_layout(const Bin& b, int esz) {
   L.x0_tiles = static_cast<int>(((b.m + 63) / 64) * static_cast<int64_t>((b.n + 63) / 64));
   L.rms_tiles = std::max(L.upd_tiles, L.x0_tiles);
   L.per_mat = static_cast<size_t>(L.prep_tiles) * 4 + static_cast<size_t>(L.rms_tiles) * 4 +
-              static_cast<size_t>(4 * L.x_elems + 2 * L.s_elems) * esz;
+              static_cast<size_t>(2 * L.x_elems + 2 * L.s_elems) * esz;
   return L;
 }
 
@@ -339,20 +339,16 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
       float* norm_part = reinterpret_cast<float*>(take(static_cast<size_t>(chunk) * L.prep_tiles * 4));
       float* rms_part = reinterpret_cast<float*>(take(static_cast<size_t>(chunk) * L.rms_tiles * 4));
       char* xr[2];
-      char* xt[2];
       const size_t xb = static_cast<size_t>(chunk) * L.x_elems * esz;
       xr[0] = take(xb);
-      xt[0] = take(xb);
       xr[1] = take(xb);
-      xt[1] = take(xb);
       char* S = take(static_cast<size_t>(chunk) * L.s_elems * esz);
       char* P = take(static_cast<size_t>(chunk) * L.s_elems * esz);
 
       {
         PrepArgs a{};
         a.desc = desc;
-        a.x_row = xr[0];
-        a.x_t = xt[0];
+        a.x = xr[0];
         a.x_stride = L.x_elems;
         a.tile = tile_size(bin.cfg);
         a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
@@ -376,8 +372,7 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
       if (h.ns_steps == 0) {
         ApplyX0Args a{};
         a.desc = desc;
-        a.x_row = xr[0];
-        a.x_t = xt[0];
+        a.x = xr[0];
         a.x_stride = L.x_elems;
         a.tile = tile_size(bin.cfg);
         a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
@@ -398,9 +393,7 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
         const double m = bin.m, n = bin.n;
         for (int k = 0; k < h.ns_steps; ++k) {
           char* xrc = xr[k & 1];
-          char* xtc = xt[k & 1];
           char* xrn = xr[(k + 1) & 1];
-          char* xtn = xt[(k + 1) & 1];
           const float* rs = k == 0 ? rscale : nullptr;
           {  // S = X X^T
             GemmArgs g{};
@@ -425,11 +418,11 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
             ProfScope ps(MO_K_POLY, s, chunk * m * m * m);
             if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_POLY, g, s), s, "poly"))) return rc;
           }
-          {  // X' = P' X
+          {  // X' = P' X, with X read K-major from its own layout
             const bool last = (k + 1 == h.ns_steps);
             GemmArgs g{};
             g.A = P;   g.sA = L.s_elems;
-            g.B = xtc; g.sB = L.x_elems;
+            g.B = xrc; g.sB = L.x_elems;
             g.M = bin.m_pad; g.N = bin.n_pad; g.K = bin.m_pad;
             g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.batch = chunk;
             g.rscale = rs;
@@ -437,7 +430,6 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
             int cls = MO_K_UPDATE;
             if (!last) {
               g.C = xrn; g.sC = L.x_elems;
-              g.Ct = xtn; g.sCt = L.x_elems;
             } else {
               g.desc = desc;
               g.m_true = bin.m; g.n_true = bin.n;

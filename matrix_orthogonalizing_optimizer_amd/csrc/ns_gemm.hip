@@ -38,6 +38,7 @@ namespace mo {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+typedef short v4s16_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -190,10 +191,34 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
 
 #define MO_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
 
+// One wave-wide direct-to-LDS load: lane l copies the 16 bytes at gptr
+// (its own address) to LDS byte address lds_base + 16 l.  Written as asm so
+// that the compiler does not track these LDS writes: it would otherwise
+// drain every load in flight before each transposing LDS read it cannot
+// disambiguate.  The main loop orders them explicitly (s_waitcnt vmcnt
+// before each barrier, vmcnt(0) before LDS is reused).  The instruction
+// writes no registers; lds_base must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(MO_LDS(p)));
+}
+
 template <typename T, int TILE, int EPI>
 __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   using E = Elem<T>;
   constexpr bool kSym = (EPI == EPI_GRAM || EPI == EPI_POLY);
+  // Products with X as the second factor (X' = P' X) read B = X in its own
+  // row-major blocked layout, i.e. K-major: stage kt is rows [32 kt, 32 kt
+  // + 32) of X restricted to this tile's columns, and fragments are taken
+  // with transposing LDS reads.  The MFMA operands are swapped for them so
+  // that each lane ends up with four consecutive columns of one row of the
+  // result (one 8- or 16-byte store).
+  constexpr bool kNN = (EPI == EPI_UPDATE || EPI == EPI_APPLY || EPI == EPI_STORE);
   constexpr int kRowBytes = 64;                   // bytes of a tile row per stage
   constexpr int BK = kRowBytes / sizeof(T);       // K elements per stage
   constexpr int CPR = kRowBytes / 16;             // 16-byte chunks per row (4)
@@ -210,7 +235,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // [TILE][kPR + 4] (oriented parameters: parameter rows = tile columns).
   constexpr bool kApply = (EPI == EPI_APPLY || EPI == EPI_STORE);
   constexpr int kPR = TILE == 256 ? 128 : TILE;
-  constexpr int kApplyFloats = TILE * (kPR + 4) > kPR * (TILE + 8) ? TILE * (kPR + 4) : kPR * (TILE + 8);
+  constexpr int kApplyFloats = TILE * (kPR + 4) > kPR * (TILE + 4) ? TILE * (kPR + 4) : kPR * (TILE + 4);
   constexpr int kSmemChunks = (kApply && kApplyFloats / 4 > NST * STAGE) ? kApplyFloats / 4 : NST * STAGE;
   __shared__ u32x4 smem[kSmemChunks];
 
@@ -226,9 +251,21 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   const int nk = p.K / BK;
   const int64_t stage_elems = static_cast<int64_t>(TILE) * BK;
   const T* __restrict__ Ag = static_cast<const T*>(p.A) + b * p.sA + static_cast<int64_t>(ti) * nk * stage_elems;
-  const T* __restrict__ Bg = static_cast<const T*>(p.B) + b * p.sB + static_cast<int64_t>(tj) * nk * stage_elems;
+  const T* __restrict__ Bg = kNN ? static_cast<const T*>(p.B) + b * p.sB
+                                  : static_cast<const T*>(p.B) + b * p.sB + static_cast<int64_t>(tj) * nk * stage_elems;
+  // K-major B: X is blocked [K / TILE panels][N / BK column stages][TILE][BK];
+  // the 32 (bf16) or 16 (fp32) rows of stage kt in column stage c form one
+  // contiguous block of BK rows x 64 bytes
+  constexpr int kSPT = TILE / BK;                 // column stages per tile
+  constexpr int kBlkBytes = BK * 64;              // bytes of one such block
+  const int nkb_b = p.N / BK;
+  auto b_koff = [&](int kt) -> int64_t {          // elements: stage kt's row block
+    const int pk = kt / kSPT, rr0 = (kt - pk * kSPT) * BK;
+    return (static_cast<int64_t>(pk) * nkb_b * TILE + rr0) * BK;
+  };
 
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int wr = (wave >> 1) * WT, wc = (wave & 1) * WT;
   const int l32 = lane & 31, lh = lane >> 5;
 
@@ -237,14 +274,29 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // wave-wide global_load_lds_dwordx4 copies 1 KiB of it (lane l moves the
   // 16 bytes at +16 l), and this wave's loads i cover 1 KiB pieces
   // wave*INST + i of the operand's block.
-  const int goff = (wave * INST) * 64 * E::kVec + lane * E::kVec;
+  // The address of a load is a wave-uniform stage base (scalar registers)
+  // plus this lane's constant 32-bit byte offset, so no per-lane 64-bit
+  // arithmetic is repeated in the main loop.
+  const uint32_t lane_bytes = static_cast<uint32_t>((wave * INST * 64 + lane) * 16);
   // load q of this wave's DPW loads of stage kt into LDS buffer buf: even q
   // are pieces of A, odd q the matching pieces of B
   auto dma1 = [&](int buf, int kt, auto q) {
     constexpr int i = decltype(q)::value / 2;
-    u32x4* st = smem + buf * STAGE + (q % 2 ? OPS : 0);
-    const T* src = (q % 2 ? Bg : Ag) + static_cast<int64_t>(kt) * stage_elems + goff + i * 64 * E::kVec;
-    __builtin_amdgcn_global_load_lds(static_cast<void*>(const_cast<T*>(src)), MO_LDS(st + (wave * INST + i) * 64), 16, 0, 0);
+    constexpr bool isB = decltype(q)::value % 2;
+    u32x4* st = smem + buf * STAGE + (isB ? OPS : 0);
+    const char* src;
+    if constexpr (kNN && isB) {
+      // piece wave*INST + i: 1 KiB of column stage (piece / (kBlkBytes / 1 KiB))
+      const int piece = wave * INST + i;
+      const int c = piece * 1024 / kBlkBytes, within = piece * 1024 - c * kBlkBytes;
+      const char* base = reinterpret_cast<const char*>(
+          Bg + b_koff(kt) + static_cast<int64_t>(tj * kSPT + c) * TILE * BK);
+      src = base + (static_cast<uint32_t>(within) + static_cast<uint32_t>(lane * 16));
+    } else {
+      const char* base = reinterpret_cast<const char*>((isB ? Bg : Ag) + static_cast<int64_t>(kt) * stage_elems);
+      src = base + (lane_bytes + static_cast<uint32_t>(i * 1024));
+    }
+    lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(st + (wave * INST + i) * 64)));
   };
   auto dma = [&](int buf, int kt) { unroll<DPW>([&](auto q) { dma1(buf, kt, q); }); };
 
@@ -261,14 +313,53 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // the other substep run.
   const int rsw = (l32 >> 2) & 3;               // slot swizzle of the rows this lane reads
   u32x4 fa[2][FM], fb[2][FM];
+  // B fragment of column block f from a K-major stage ([kSPT][BK rows][BK],
+  // chunks permuted per row): this lane's column n = wc + 32 f + l32 and its
+  // K values of substep ks.
+  //   bf16: two ds_read_b64_tr_b16, four K each.  Within each 16-lane group
+  //   lane i points at row k0 + i / 4, columns n0 + 4 (i % 4) .. + 3, and the
+  //   read returns to lane i the four rows k0 .. k0 + 3 of column n0 + i.
+  //   fp32: the four K values of the lane's chunk one by one.
+  auto frag_kmajor = [&](const T* sB, auto ks, auto f) -> u32x4 {
+    constexpr int F = decltype(f)::value, KS = decltype(ks)::value;
+    auto at = [&](int k, int n) {                 // element offset of (k, n) in the stage
+      const int c = n / BK, c2 = n - c * BK, ch = c2 / E::kVec;
+      return c * BK * BK + k * BK + ((ch ^ ((k >> 2) & 3)) * E::kVec) + (c2 - ch * E::kVec);
+    };
+    u32x4 r;
+    if constexpr (sizeof(T) == 2) {
+      const int gi = lane & 15;
+      const int n = wc + 32 * F + (l32 & 16) + 4 * (gi & 3);
+      unroll<2>([&](auto h) {
+        const int k = KS * 16 + 8 * lh + 4 * decltype(h)::value + (gi >> 2);
+        const v4s16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s16_t*)(sB + at(k, n)));
+        const uint2 u = __builtin_bit_cast(uint2, v);
+        r[2 * decltype(h)::value] = u.x;
+        r[2 * decltype(h)::value + 1] = u.y;
+      });
+    } else {
+      const int n = wc + 32 * F + l32;
+      unroll<4>([&](auto t) {
+        const int k = (KS * 2 + lh) * 4 + decltype(t)::value;
+        r[decltype(t)::value] = __float_as_uint(reinterpret_cast<const float*>(sB)[at(k, n)]);
+      });
+    }
+    return r;
+  };
   // fragment read q of substep ks into register set `set`: even q read A
   // fragments, odd q B fragments
   auto frag1 = [&](int buf, auto ks, auto set, auto q) {
     constexpr int f = decltype(q)::value / 2;
     const u32x4* sA = smem + buf * STAGE;
     const int slot = (ks * 2 + lh) ^ rsw;
-    if constexpr (decltype(q)::value % 2 == 0) fa[set][f] = sA[(wr + f * 32 + l32) * CPR + slot];
-    else fb[set][f] = sA[OPS + (wc + f * 32 + l32) * CPR + slot];
+    if constexpr (decltype(q)::value % 2 == 0) {
+      fa[set][f] = sA[(wr + f * 32 + l32) * CPR + slot];
+    } else if constexpr (!kNN) {
+      fb[set][f] = sA[OPS + (wc + f * 32 + l32) * CPR + slot];
+    } else {
+      fb[set][f] = frag_kmajor(reinterpret_cast<const T*>(sA + OPS), ks, std::integral_constant<int, f>{});
+    }
   };
   constexpr int kGroups = FM * FM;              // MFMA groups (E::mma) per substep
   constexpr int kReads = 2 * FM;                // fragment reads per substep
@@ -281,7 +372,10 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     constexpr int kLd = std::decay_t<decltype(nld)>::value;
     unroll<kGroups>([&](auto g) {
       constexpr int G = decltype(g)::value;
-      acc[G / FM][G % FM] = E::mma(fa[set][G / FM], fb[set][G % FM], acc[G / FM][G % FM]);
+      if constexpr (kNN)
+        acc[G / FM][G % FM] = E::mma(fb[set][G % FM], fa[set][G / FM], acc[G / FM][G % FM]);
+      else
+        acc[G / FM][G % FM] = E::mma(fa[set][G / FM], fb[set][G % FM], acc[G / FM][G % FM]);
       constexpr int r0 = kReads <= kGroups ? G : G * kReads / kGroups;
       constexpr int r1 = kReads <= kGroups ? (G < kReads ? G + 1 : G) : (G + 1) * kReads / kGroups;
       unroll<r1 - r0>([&](auto k) { rd(std::integral_constant<int, r0 + decltype(k)::value>{}); });
@@ -368,7 +462,27 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     }
   };
 
-  if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY || EPI == EPI_UPDATE) {
+  if constexpr (EPI == EPI_UPDATE) {
+    // X' = s acc.  The swapped MFMA operands leave in register r of block
+    // (i, j) the element at row wr + 32 i + l32, column wc + 32 j + 8 q + 4 lh
+    // + e of the tile (q = r / 4, e = r % 4): four consecutive columns, one
+    // store into the LDS copy of the tile, then one coalesced copy-out.
+    int on[4];
+    unroll<4>([&](auto q) { on[q] = loff(wr + l32, wc + 8 * q + 4 * lh); });
+    unroll<FM>([&](auto i) {
+      unroll<FM>([&](auto j) {
+        unroll<4>([&](auto q) {
+          constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+          const int o = on[Q] + 32 * I * BK + (32 * J / BK) * TILE * BK;
+          E::store4(lt + o, s * acc[I][J][4 * Q], s * acc[I][J][4 * Q + 1], s * acc[I][J][4 * Q + 2],
+                    s * acc[I][J][4 * Q + 3]);
+        });
+      });
+    });
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    copy_out(C + blk_tile(Lc, ti, tj));
+  } else if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
     // Accumulator element (i, j, r) sits at tile row wr + 32 i + 8 q + 4 lh
     // + e (q = r / 4, e = r % 4) and column wc + 32 j + l32.  Its LDS offset
     // is a per-lane base plus a compile-time displacement:
@@ -439,10 +553,10 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     }
 
     // transposed pass: value (rr, cc) to LDS position (cc, rr), four rows of
-    // a lane in one store.  This is the mirror tile (symmetric products) or
-    // the tile of X'^T (update); on a diagonal tile it puts every value at
-    // its mirror position and the direct pass below then overwrites the
-    // lower triangle, leaving the tile exactly symmetric.
+    // a lane in one store.  This is the mirror tile; on a diagonal tile it
+    // puts every value at its mirror position and the direct pass below
+    // then overwrites the lower triangle, leaving the tile exactly
+    // symmetric.
     unroll<FM>([&](auto i) {
       unroll<FM>([&](auto j) {
         unroll<4>([&](auto q) {
@@ -455,12 +569,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
     if (!diag) {
-      if constexpr (EPI == EPI_UPDATE) {
-        const Blocked Lt = blocked(TILE, p.M, sizeof(T));  // Ct: [N, M]
-        copy_out(static_cast<T*>(p.Ct) + b * p.sCt + blk_tile(Lt, tj, ti));
-      } else {
-        copy_out(C + blk_tile(Lc, tj, ti));
-      }
+      copy_out(C + blk_tile(Lc, tj, ti));
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       barrier();
     }
@@ -509,105 +618,130 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     const int64_t ldw = ori ? p.m_true : p.n_true;         // parameter row length
     const int wrows = ori ? p.n_true : p.m_true;            // parameter rows
     const float lrwd = p.lrwd, stp = p.step;
-    float* __restrict__ W = md.param;
-    T* __restrict__ O = EPI == EPI_STORE ? static_cast<T*>(p.out) + b * p.s_out : nullptr;
+    // global address space: plain global loads and stores, not flat ones
+    typedef __attribute__((address_space(1))) float gfloat;
+    typedef __attribute__((address_space(1))) T gT;
+    gfloat* __restrict__ W = (gfloat*)md.param;
+    gT* __restrict__ O = EPI == EPI_STORE ? (gT*)(static_cast<T*>(p.out) + b * p.s_out) : nullptr;
     float* const lf = reinterpret_cast<float*>(smem);
-    // padded LDS row lengths: the lh = 1 half-wave writes 4 rows below the
-    // lh = 0 half, 32 banks away
-    constexpr int kLd = TILE + 8, kLdT = kPR + 4;
+    // padded LDS row lengths (consecutive lanes write consecutive rows)
+    constexpr int kLd = TILE + 4, kLdT = kPR + 4;
     const bool full = (ti + 1) * TILE <= p.m_true && (tj + 1) * TILE <= p.n_true && (ldw % 4) == 0;
     float sq = 0.0f;
-    auto apply4 = [&](int64_t off, int wcol, const float (&x)[4]) {
-      if (full) {
-        if constexpr (EPI == EPI_APPLY) {
-          float4 w = *reinterpret_cast<const float4*>(W + off);
-          w.x = w.x - (lrwd * w.x + stp * x[0]);
-          w.y = w.y - (lrwd * w.y + stp * x[1]);
-          w.z = w.z - (lrwd * w.z + stp * x[2]);
-          w.w = w.w - (lrwd * w.w + stp * x[3]);
-          *reinterpret_cast<float4*>(W + off) = w;
-        } else {
-          E::store4(O + off, x[0], x[1], x[2], x[3]);
-        }
-        sq += (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
+    using True = std::integral_constant<bool, true>;
+    using False = std::integral_constant<bool, false>;
+    // x of this wave's accumulator blocks whose rows fall in pass `pc` into
+    // LDS: [kPR][kLd] rows of W, or [TILE][kLdT] (oriented: W rows are tile
+    // columns).  Lane l32 holds row 32 i + l32 and four consecutive columns.
+    auto stage = [&](auto pc, auto oric) {
+      constexpr int pass = decltype(pc)::value;
+      constexpr bool kOri = decltype(oric)::value;
+      const int r_base = wr - pass * kPR;
+      unroll<FM>([&](auto i) {
+        unroll<FM>([&](auto j) {
+          unroll<4>([&](auto q) {
+            constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+            const int rr = r_base + 32 * I + l32;
+            const int cc = wc + 32 * J + 8 * Q + 4 * lh;
+            const float x0 = s * acc[I][J][4 * Q], x1 = s * acc[I][J][4 * Q + 1];
+            const float x2 = s * acc[I][J][4 * Q + 2], x3 = s * acc[I][J][4 * Q + 3];
+            if constexpr (kOri) {
+              lf[(cc + 0) * kLdT + rr] = x0;
+              lf[(cc + 1) * kLdT + rr] = x1;
+              lf[(cc + 2) * kLdT + rr] = x2;
+              lf[(cc + 3) * kLdT + rr] = x3;
+            } else {
+              *reinterpret_cast<float4*>(lf + rr * kLd + cc) = make_float4(x0, x1, x2, x3);
+            }
+          });
+        });
+      });
+    };
+    // Group g of a pass: four elements consecutive along one parameter row.
+    // Returns the LDS offset; sets the parameter row and column.
+    auto group = [&](auto pc, auto oric, int g, int& wrow, int& wcol) {
+      constexpr int pass = decltype(pc)::value;
+      if constexpr (decltype(oric)::value) {
+        const int cc = g / (kPR / 4), r4 = (g % (kPR / 4)) * 4;
+        wrow = tj * TILE + cc;
+        wcol = ti * TILE + pass * kPR + r4;
+        return cc * kLdT + r4;
       } else {
+        const int r = g / (TILE / 4), c4 = (g % (TILE / 4)) * 4;
+        wrow = ti * TILE + pass * kPR + r;
+        wcol = tj * TILE + c4;
+        return r * kLd + c4;
+      }
+    };
+    constexpr int kGroups = kPR * TILE / 4;                 // groups per pass
+    constexpr int kU = kGroups >= 256 * 8 ? 8 : kGroups / 256;
+    static_assert(kGroups % (256 * kU) == 0, "group loop");
+    // whole tile inside the parameter, rows a multiple of 4: all of a step's
+    // loads (LDS x, W) are issued before any store
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) f32x4_t gf4;
+    auto copy_full = [&](auto pc, auto oric) {
+#pragma unroll 1
+      for (int g0 = 0; g0 < kGroups; g0 += 256 * kU) {
+        f32x4_t xv[kU], wv[kU];
+        int64_t off[kU];
+        unroll<kU>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          int wrow, wcol;
+          const int lo = group(pc, oric, g0 + U * 256 + tid, wrow, wcol);
+          off[U] = static_cast<int64_t>(wrow) * ldw + wcol;
+          xv[U] = *reinterpret_cast<const f32x4_t*>(lf + lo);
+          if constexpr (EPI == EPI_APPLY) wv[U] = *(const gf4*)(W + off[U]);
+        });
+        unroll<kU>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          const f32x4_t x = xv[U];
+          if constexpr (EPI == EPI_APPLY) {
+            const f32x4_t w = wv[U];
+            *(gf4*)(W + off[U]) = w - (lrwd * w + stp * x);
+          } else {
+            E::store4((T*)(O + off[U]), x[0], x[1], x[2], x[3]);
+          }
+          sq += (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
+        });
+      }
+    };
+    // ragged tile or row length not a multiple of 4: element by element
+    auto copy_edge = [&](auto pc, auto oric) {
+#pragma unroll 1
+      for (int g = tid; g < kGroups; g += 256) {
+        int wrow, wcol;
+        const int lo = group(pc, oric, g, wrow, wcol);
+        if (wrow >= wrows) continue;
+        const int64_t off = static_cast<int64_t>(wrow) * ldw + wcol;
         unroll<4>([&](auto k) {
           constexpr int K = decltype(k)::value;
           if (wcol + K < ldw) {
+            const float x = lf[lo + K];
             if constexpr (EPI == EPI_APPLY) {
               const float w = W[off + K];
-              W[off + K] = w - (lrwd * w + stp * x[K]);
+              W[off + K] = w - (lrwd * w + stp * x);
             } else {
-              E::st(O + off + K, x[K]);
+              E::st((T*)(O + off + K), x);
             }
-            sq += x[K] * x[K];
+            sq += x * x;
           }
         });
       }
     };
     constexpr int kNP = TILE / kPR;
-    unroll<kNP>([&](auto pc) {
-      constexpr int pass = decltype(pc)::value;
-      if (pass > 0) barrier();                              // previous pass fully read
-      if (wr / kPR == pass) {
-        const int r_base = wr - pass * kPR;
-        unroll<FM>([&](auto i) {
-          unroll<FM>([&](auto j) {
-            unroll<4>([&](auto q) {
-              constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
-              const int rr = r_base + 32 * I + 8 * Q + 4 * lh;  // tile row (within the pass) of e = 0
-              const int cc = wc + 32 * J + l32;
-              const float x0 = s * acc[I][J][4 * Q], x1 = s * acc[I][J][4 * Q + 1];
-              const float x2 = s * acc[I][J][4 * Q + 2], x3 = s * acc[I][J][4 * Q + 3];
-              if (ori) {
-                *reinterpret_cast<float4*>(lf + cc * kLdT + rr) = make_float4(x0, x1, x2, x3);
-              } else {
-                lf[(rr + 0) * kLd + cc] = x0;
-                lf[(rr + 1) * kLd + cc] = x1;
-                lf[(rr + 2) * kLd + cc] = x2;
-                lf[(rr + 3) * kLd + cc] = x3;
-              }
-            });
-          });
-        });
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      barrier();
-      constexpr int kGroups = kPR * TILE / 4;
-      static_assert(kGroups % (256 * 4) == 0 || kGroups < 256 * 4, "group loop");
-      constexpr int kU = kGroups >= 256 * 4 ? 4 : 1;
-#pragma unroll 1
-      for (int g0 = 0; g0 < kGroups; g0 += 256 * kU) {
-        float x[kU][4];
-        int64_t off[kU];
-        int wcol[kU];
-        bool rowok[kU];
-        unroll<kU>([&](auto u) {
-          constexpr int U = decltype(u)::value;
-          const int g = g0 + U * 256 + tid;
-          int lo, wrow;
-          if (ori) {              // parameter row = tile column
-            const int cc = g / (kPR / 4), r4 = (g % (kPR / 4)) * 4;
-            lo = cc * kLdT + r4;
-            wrow = tj * TILE + cc;
-            wcol[U] = ti * TILE + pass * kPR + r4;
-          } else {
-            const int r = g / (TILE / 4), c4 = (g % (TILE / 4)) * 4;
-            lo = r * kLd + c4;
-            wrow = ti * TILE + pass * kPR + r;
-            wcol[U] = tj * TILE + c4;
-          }
-          const float4 v = *reinterpret_cast<const float4*>(lf + lo);
-          x[U][0] = v.x; x[U][1] = v.y; x[U][2] = v.z; x[U][3] = v.w;
-          rowok[U] = wrow < wrows && wcol[U] < ldw;
-          off[U] = static_cast<int64_t>(wrow) * ldw + wcol[U];
-        });
-        unroll<kU>([&](auto u) {
-          constexpr int U = decltype(u)::value;
-          if (rowok[U]) apply4(off[U], wcol[U], x[U]);
-        });
-      }
-    });
+    auto run = [&](auto oric) {
+      unroll<kNP>([&](auto pc) {
+        if (decltype(pc)::value > 0) barrier();             // previous pass fully read
+        if (wr / kPR == decltype(pc)::value) stage(pc, oric);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        barrier();
+        if (full) copy_full(pc, oric);
+        else copy_edge(pc, oric);
+      });
+    };
+    if (ori) run(True{});
+    else run(False{});
     if (p.rms_part) {
       // block reduction of the squared update (deterministic, no atomics)
 #pragma unroll
