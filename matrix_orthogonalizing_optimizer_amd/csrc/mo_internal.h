@@ -59,21 +59,34 @@ enum Epi : int {
 
 // All matrices are in the blocked layout (mo_layout.h) with panels of
 // TILE rows; s* are per-batch-entry strides in elements.
-struct GemmArgs {
+//
+// One launch covers up to kMaxGroup shape groups (bins) at once: GemmBin
+// holds what differs between them.  Each group's tiles are split evenly
+// over the 8 XCDs (a contiguous range per XCD, for L2 reuse), and each XCD
+// walks the groups in its own rotated order, so that tiles of different
+// lengths -- and their output bursts -- overlap across the chip.
+constexpr int kMaxGroup = 8;
+struct GemmBin {
   const void* A;  int64_t sA;            // [M, K] per batch entry
   const void* B;  int64_t sB;            // [N, K]; [K, N] for EPI_UPDATE/APPLY/STORE
   const void* D;  int64_t sD;            // [M, N] epilogue operand
   void* C;        int64_t sC;            // [M, N] output
+  const float* rscale;                   // per batch entry (applied if use_rscale)
+  const MatDesc* desc;                   // EPI_APPLY / EPI_STORE, per batch entry
+  void* out;  int64_t s_out;             // EPI_STORE output base, stride
+  float* rms_part;                       // [batch][tiles_per_mat] or null
   int M, N, K;                           // padded sizes (tile multiples)
   int tiles_m, tiles_n, tiles_per_mat, batch;
-  const float* rscale;                   // per batch entry, or null (s = 1)
-  float alpha, beta, gamma;              // EPI_POLY coefficients
-  // EPI_APPLY / EPI_STORE
-  const MatDesc* desc;                   // per batch entry
-  void* out;  int64_t s_out;             // EPI_STORE output base, stride
   int m_true, n_true;
-  float lrwd, step;                      // W <- W - (lrwd W + step x)
-  float* rms_part;                       // [batch][tiles_per_mat] or null
+  float step;                            // EPI_APPLY: W <- W - (lrwd W + step x)
+};
+struct GemmArgs {
+  GemmBin bin[kMaxGroup];
+  int nbins;
+  int per_xcd;                           // grid = 8 * per_xcd
+  int use_rscale;                        // first iteration: scale by rscale
+  float alpha, beta, gamma;              // EPI_POLY coefficients
+  float lrwd;                            // EPI_APPLY
 };
 
 // Elementwise apply for ns_steps = 0 (X_N = X_0), and for EPI_STORE with 0

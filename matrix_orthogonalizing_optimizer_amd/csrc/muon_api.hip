@@ -257,7 +257,6 @@ int build_plan(const mo_tensor* t, int64_t count, int grad_dt, int mom_dt, int n
 struct BinLayout {
   int64_t x_elems, s_elems;
   int prep_tiles, upd_tiles, x0_tiles, rms_tiles;
-  size_t per_mat;          // bytes per matrix in the chunk region
 };
 
 BinLayout bin_layout(const Bin& b, int esz) {
@@ -269,8 +268,6 @@ BinLayout bin_layout(const Bin& b, int esz) {
   L.upd_tiles = (b.m_pad / T) * (b.n_pad / T);
   L.x0_tiles = static_cast<int>(((b.m + 63) / 64) * static_cast<int64_t>((b.n + 63) / 64));
   L.rms_tiles = std::max(L.upd_tiles, L.x0_tiles);
-  L.per_mat = static_cast<size_t>(L.prep_tiles) * 4 + static_cast<size_t>(L.rms_tiles) * 4 +
-              static_cast<size_t>(2 * L.x_elems + 2 * L.s_elems) * esz;
   return L;
 }
 
@@ -278,18 +275,27 @@ size_t fixed_bytes(const HostPlan& p, bool with_table) {
   size_t f = 0;
   if (with_table) f += align_up(p.descs.size() * sizeof(MatDesc));
   f += align_up(static_cast<size_t>(p.count) * 4);
-  return f + 8 * kAlign;   // alignment slack of the chunk regions
+  return f;
 }
 
+// Bytes of an item's region (every piece rounded up to kAlign).
+size_t item_bytes(const BinLayout& L, int chunk, int esz) {
+  const size_t c = static_cast<size_t>(chunk);
+  return align_up(c * L.prep_tiles * 4) + align_up(c * L.rms_tiles * 4) +
+         2 * align_up(c * L.x_elems * esz) + 2 * align_up(c * L.s_elems * esz);
+}
+
+// full: every shape group resident at once (grouped launches); min: one
+// matrix of the largest group at a time.
 void ws_sizes(const HostPlan& p, bool with_table, size_t* full, size_t* mn) {
-  size_t mx_full = 0, mx_min = 0;
+  size_t sum_full = 0, mx_min = 0;
   for (const Bin& b : p.bins) {
     const BinLayout L = bin_layout(b, p.esz());
-    mx_full = std::max(mx_full, L.per_mat * b.count);
-    mx_min = std::max(mx_min, L.per_mat);
+    sum_full += item_bytes(L, b.count, p.esz());
+    mx_min = std::max(mx_min, item_bytes(L, 1, p.esz()));
   }
   const size_t f = fixed_bytes(p, with_table);
-  if (full) *full = f + mx_full;
+  if (full) *full = f + sum_full;
   if (mn) *mn = f + mx_min;
 }
 
@@ -308,157 +314,254 @@ int validate_hyper(const Hyper& h) {
   return MO_OK;
 }
 
+// The matrices of one shape group (or a chunk of them) and their carved
+// workspace: [norm partials] [rms partials] [X] [X'] [S] [P].
+struct Item {
+  const Bin* bin;
+  BinLayout L;
+  int c0, chunk;
+  const MatDesc* desc;
+  float* rscale;
+  float* norm_part;
+  float* rms_part;
+  char* x[2];
+  char* S;
+  char* P;
+};
+
+char* carve(Item& it, char* q, int esz) {
+  auto take = [&](size_t bytes) {
+    char* r = q;
+    q += align_up(bytes);
+    return r;
+  };
+  const size_t c = static_cast<size_t>(it.chunk);
+  it.norm_part = reinterpret_cast<float*>(take(c * it.L.prep_tiles * 4));
+  it.rms_part = reinterpret_cast<float*>(take(c * it.L.rms_tiles * 4));
+  it.x[0] = take(c * it.L.x_elems * esz);
+  it.x[1] = take(c * it.L.x_elems * esz);
+  it.S = take(c * it.L.s_elems * esz);
+  it.P = take(c * it.L.s_elems * esz);
+  return q;
+}
+
+struct StepCtx {
+  const HostPlan& plan;
+  const Hyper& h;
+  float* update_rms;
+  hipStream_t s;
+  void* store_out;
+  int64_t store_stride;
+  int esz;
+  float lrwd;
+};
+
+float item_step(const StepCtx& c, const Item& it) {
+  const double scale = static_cast<double>(c.h.rms_scale) * std::sqrt(static_cast<double>(it.bin->n));
+  return static_cast<float>(static_cast<double>(c.h.lr) * scale);
+}
+
+// One Newton-Schulz product over a set of items: launches grouped by tile
+// configuration, up to kMaxGroup shape groups per launch.
+int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int cls, const char* what) {
+  int rc;
+  const int N = c.h.ns_steps;
+  std::vector<int> order(items.size());
+  for (size_t i = 0; i < items.size(); ++i) order[i] = static_cast<int>(i);
+  // same tile configuration together
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return items[x].bin->cfg < items[y].bin->cfg; });
+  size_t i0 = 0;
+  while (i0 < order.size()) {
+    const TileCfg cfg = items[order[i0]].bin->cfg;
+    size_t i1 = i0;
+    while (i1 < order.size() && items[order[i1]].bin->cfg == cfg && i1 - i0 < static_cast<size_t>(kMaxGroup)) ++i1;
+    GemmArgs g{};
+    g.nbins = static_cast<int>(i1 - i0);
+    g.use_rscale = (k == 0 && (epi == EPI_GRAM || epi == EPI_UPDATE || epi == EPI_APPLY || epi == EPI_STORE)) ? 1 : 0;
+    g.alpha = c.h.c; g.beta = c.h.b; g.gamma = c.h.a;
+    g.lrwd = c.lrwd;
+    double work = 0.0;
+    int per_xcd = 0;
+    const bool want_rms = c.update_rms != nullptr && c.store_out == nullptr;
+    for (size_t j = i0; j < i1; ++j) {
+      const Item& it = items[order[j]];
+      const Bin& bin = *it.bin;
+      GemmBin& gb = g.bin[j - i0];
+      const int T = tile_size(bin.cfg);
+      const int tm = bin.m_pad / T, tn = bin.n_pad / T;
+      const double m = bin.m, n = bin.n;
+      char* xc = it.x[k & 1];
+      char* xn = it.x[(k + 1) & 1];
+      gb.rscale = it.rscale;
+      gb.batch = it.chunk;
+      if (epi == EPI_GRAM) {            // S = X X^T
+        gb.A = xc; gb.sA = it.L.x_elems;
+        gb.B = xc; gb.sB = it.L.x_elems;
+        gb.C = it.S; gb.sC = it.L.s_elems;
+        gb.M = bin.m_pad; gb.N = bin.m_pad; gb.K = bin.n_pad;
+        gb.tiles_m = tm; gb.tiles_n = tm; gb.tiles_per_mat = tm * (tm + 1) / 2;
+        work += it.chunk * m * m * n;
+      } else if (epi == EPI_POLY) {     // P' = a I + b S + c S S
+        gb.A = it.S; gb.sA = it.L.s_elems;
+        gb.B = it.S; gb.sB = it.L.s_elems;
+        gb.D = it.S; gb.sD = it.L.s_elems;
+        gb.C = it.P; gb.sC = it.L.s_elems;
+        gb.M = bin.m_pad; gb.N = bin.m_pad; gb.K = bin.m_pad;
+        gb.tiles_m = tm; gb.tiles_n = tm; gb.tiles_per_mat = tm * (tm + 1) / 2;
+        work += it.chunk * m * m * m;
+      } else {                          // X' = P' X, X read K-major from its own layout
+        gb.A = it.P; gb.sA = it.L.s_elems;
+        gb.B = xc; gb.sB = it.L.x_elems;
+        gb.M = bin.m_pad; gb.N = bin.n_pad; gb.K = bin.m_pad;
+        gb.tiles_m = tm; gb.tiles_n = tn; gb.tiles_per_mat = tm * tn;
+        if (epi == EPI_UPDATE) {
+          gb.C = xn; gb.sC = it.L.x_elems;
+        } else {
+          gb.desc = it.desc;
+          gb.m_true = bin.m; gb.n_true = bin.n;
+          gb.step = item_step(c, it);
+          gb.rms_part = want_rms ? it.rms_part : nullptr;
+          if (epi == EPI_STORE) {
+            gb.out = static_cast<char*>(c.store_out) + static_cast<size_t>(it.c0) * c.store_stride * c.esz;
+            gb.s_out = c.store_stride;
+          }
+        }
+        work += 2.0 * it.chunk * m * m * n;
+      }
+      const int total = gb.tiles_per_mat * gb.batch;
+      per_xcd += (total + 7) / 8;
+    }
+    g.per_xcd = per_xcd;
+    (void)N;
+    ProfScope ps(cls, c.s, work);
+    if ((rc = checked(launch_gemm(c.plan.ns_dt, cfg, epi, g, c.s), c.s, what))) return rc;
+    i0 = i1;
+  }
+  return MO_OK;
+}
+
+// Momentum, norm, Newton-Schulz and apply for a set of items processed
+// together (all shape groups at once when the workspace allows).
+int run_round(const StepCtx& c, std::vector<Item>& items) {
+  int rc;
+  const HostPlan& plan = c.plan;
+  const Hyper& h = c.h;
+  const bool want_rms = c.update_rms != nullptr && c.store_out == nullptr;
+  for (Item& it : items) {
+    const Bin& bin = *it.bin;
+    PrepArgs a{};
+    a.desc = it.desc;
+    a.x = it.x[0];
+    a.x_stride = it.L.x_elems;
+    a.tile = tile_size(bin.cfg);
+    a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
+    a.tiles_per_mat = it.L.prep_tiles;
+    a.mu = h.mu;
+    a.nesterov = h.nesterov;
+    a.has_mom = h.has_mom ? 1 : 0;
+    a.grad_dt = plan.grad_dt; a.mom_dt = plan.mom_dt; a.ns_dt = plan.ns_dt;
+    a.norm_part = it.norm_part;
+    const double elems = static_cast<double>(it.chunk) * bin.m * bin.n;
+    const double bytes = elems * (dt_size(plan.grad_dt) + (h.has_mom ? 2 * dt_size(plan.mom_dt) : 0) + c.esz);
+    {
+      ProfScope ps(MO_K_MOMENTUM, c.s, bytes);
+      if ((rc = checked(launch_prep(a, it.chunk, c.s), c.s, "prep"))) return rc;
+    }
+    NormArgs na{it.norm_part, it.L.prep_tiles, h.eps, it.rscale};
+    ProfScope ps(MO_K_NORM, c.s, static_cast<double>(it.chunk) * it.L.prep_tiles * 4);
+    if ((rc = checked(launch_norm(na, it.chunk, c.s), c.s, "norm"))) return rc;
+  }
+  if (h.ns_steps == 0) {
+    for (Item& it : items) {
+      const Bin& bin = *it.bin;
+      ApplyX0Args a{};
+      a.desc = it.desc;
+      a.x = it.x[0];
+      a.x_stride = it.L.x_elems;
+      a.tile = tile_size(bin.cfg);
+      a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
+      a.tiles_per_mat = it.L.x0_tiles;
+      a.rscale = it.rscale;
+      a.lrwd = c.lrwd;
+      a.step = item_step(c, it);
+      a.ns_dt = plan.ns_dt;
+      a.out = c.store_out ? static_cast<char*>(c.store_out) + static_cast<size_t>(it.c0) * c.store_stride * c.esz
+                          : nullptr;
+      a.s_out = c.store_stride;
+      a.rms_part = want_rms ? it.rms_part : nullptr;
+      const double elems = static_cast<double>(it.chunk) * bin.m * bin.n;
+      ProfScope ps(MO_K_APPLY_X0, c.s, elems * (c.esz + (c.store_out ? c.esz : 8)));
+      if ((rc = checked(launch_apply_x0(a, it.chunk, c.s), c.s, "apply_x0"))) return rc;
+    }
+  } else {
+    for (int k = 0; k < h.ns_steps; ++k) {
+      const bool last = (k + 1 == h.ns_steps);
+      if ((rc = gemm_phase(c, items, EPI_GRAM, k, MO_K_GRAM, "gram"))) return rc;
+      if ((rc = gemm_phase(c, items, EPI_POLY, k, MO_K_POLY, "poly"))) return rc;
+      const Epi ue = !last ? EPI_UPDATE : (c.store_out ? EPI_STORE : EPI_APPLY);
+      if ((rc = gemm_phase(c, items, ue, k, last ? MO_K_APPLY : MO_K_UPDATE, "update"))) return rc;
+    }
+  }
+  if (want_rms) {
+    for (Item& it : items) {
+      RmsArgs a{};
+      a.desc = it.desc;
+      a.part = it.rms_part;
+      a.tiles = h.ns_steps == 0 ? it.L.x0_tiles : it.L.upd_tiles;
+      a.inv_count = 1.0 / (static_cast<double>(it.bin->m) * it.bin->n);
+      a.update_rms = c.update_rms;
+      ProfScope ps(MO_K_RMS, c.s, static_cast<double>(it.chunk) * a.tiles * 4);
+      if ((rc = checked(launch_rms(a, it.chunk, c.s), c.s, "rms"))) return rc;
+    }
+  }
+  return MO_OK;
+}
+
 // Enqueues the whole step.  `d_desc` is the device copy of plan.descs.
 // `store_out`: Newton-Schulz-only mode, writing X_N into store_out.
+// With a workspace of the full size every shape group is resident at once
+// and each Newton-Schulz product is one launch over all groups; otherwise
+// the groups (in chunks that fit) are processed one after another.
 int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float* update_rms, char* ws,
              size_t ws_bytes, size_t fixed_used, hipStream_t s, void* store_out, int64_t store_stride) {
   const int esz = plan.esz();
   float* rscale_all = reinterpret_cast<float*>(ws + fixed_used);
   char* region = ws + fixed_used + align_up(static_cast<size_t>(plan.count) * 4);
-  // every chunk region is carved into 8 pieces, each rounded up to kAlign
-  const size_t region_bytes = ws_bytes - static_cast<size_t>(region - ws) - 8 * kAlign;
+  const size_t region_bytes = ws_bytes - static_cast<size_t>(region - ws);
+  StepCtx c{plan, h, update_rms, s, store_out, store_stride, esz,
+            static_cast<float>(static_cast<double>(h.lr) * h.wd)};
+  auto make_item = [&](const Bin& bin, int c0, int chunk) {
+    Item it{};
+    it.bin = &bin;
+    it.L = bin_layout(bin, esz);
+    it.c0 = c0;
+    it.chunk = chunk;
+    it.desc = d_desc + bin.first + c0;
+    it.rscale = rscale_all + bin.first + c0;
+    return it;
+  };
+  size_t all = 0;
+  for (const Bin& bin : plan.bins) all += item_bytes(bin_layout(bin, esz), bin.count, esz);
+  if (all <= region_bytes) {
+    std::vector<Item> items;
+    char* q = region;
+    for (const Bin& bin : plan.bins) {
+      items.push_back(make_item(bin, 0, bin.count));
+      q = carve(items.back(), q, esz);
+    }
+    return run_round(c, items);
+  }
   int rc;
   for (const Bin& bin : plan.bins) {
     const BinLayout L = bin_layout(bin, esz);
-    const int cap = static_cast<int>(std::min<size_t>(bin.count, region_bytes / L.per_mat));
+    int cap = bin.count;
+    while (cap > 0 && item_bytes(L, cap, esz) > region_bytes) --cap;
     if (cap < 1) return fail(MO_EWORKSPACE, "workspace too small for a %d x %d matrix", bin.m, bin.n);
-    const double scale = static_cast<double>(h.rms_scale) * std::sqrt(static_cast<double>(bin.n));
-    const float step = static_cast<float>(static_cast<double>(h.lr) * scale);
-    const float lrwd = static_cast<float>(static_cast<double>(h.lr) * h.wd);
     for (int c0 = 0; c0 < bin.count; c0 += cap) {
-      const int chunk = std::min(cap, bin.count - c0);
-      const MatDesc* desc = d_desc + bin.first + c0;
-      float* rscale = rscale_all + bin.first + c0;
-      // carve the chunk region
-      char* q = region;
-      auto take = [&](size_t bytes) {
-        char* r = q;
-        q += align_up(bytes);
-        return r;
-      };
-      float* norm_part = reinterpret_cast<float*>(take(static_cast<size_t>(chunk) * L.prep_tiles * 4));
-      float* rms_part = reinterpret_cast<float*>(take(static_cast<size_t>(chunk) * L.rms_tiles * 4));
-      char* xr[2];
-      const size_t xb = static_cast<size_t>(chunk) * L.x_elems * esz;
-      xr[0] = take(xb);
-      xr[1] = take(xb);
-      char* S = take(static_cast<size_t>(chunk) * L.s_elems * esz);
-      char* P = take(static_cast<size_t>(chunk) * L.s_elems * esz);
-
-      {
-        PrepArgs a{};
-        a.desc = desc;
-        a.x = xr[0];
-        a.x_stride = L.x_elems;
-        a.tile = tile_size(bin.cfg);
-        a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
-        a.tiles_per_mat = L.prep_tiles;
-        a.mu = h.mu;
-        a.nesterov = h.nesterov;
-        a.has_mom = h.has_mom ? 1 : 0;
-        a.grad_dt = plan.grad_dt; a.mom_dt = plan.mom_dt; a.ns_dt = plan.ns_dt;
-        a.norm_part = norm_part;
-        const double elems = static_cast<double>(chunk) * bin.m * bin.n;
-        const double bytes = elems * (dt_size(plan.grad_dt) + (h.has_mom ? 2 * dt_size(plan.mom_dt) : 0) + esz);
-        ProfScope ps(MO_K_MOMENTUM, s, bytes);
-        if ((rc = checked(launch_prep(a, chunk, s), s, "prep"))) return rc;
-      }
-      {
-        NormArgs a{norm_part, L.prep_tiles, h.eps, rscale};
-        ProfScope ps(MO_K_NORM, s, static_cast<double>(chunk) * L.prep_tiles * 4);
-        if ((rc = checked(launch_norm(a, chunk, s), s, "norm"))) return rc;
-      }
-      const bool want_rms = update_rms != nullptr && store_out == nullptr;
-      if (h.ns_steps == 0) {
-        ApplyX0Args a{};
-        a.desc = desc;
-        a.x = xr[0];
-        a.x_stride = L.x_elems;
-        a.tile = tile_size(bin.cfg);
-        a.m = bin.m; a.n = bin.n; a.m_pad = bin.m_pad; a.n_pad = bin.n_pad;
-        a.tiles_per_mat = L.x0_tiles;
-        a.rscale = rscale;
-        a.lrwd = lrwd;
-        a.step = step;
-        a.ns_dt = plan.ns_dt;
-        a.out = store_out ? static_cast<char*>(store_out) + static_cast<size_t>(c0) * store_stride * esz : nullptr;
-        a.s_out = store_stride;
-        a.rms_part = want_rms ? rms_part : nullptr;
-        const double elems = static_cast<double>(chunk) * bin.m * bin.n;
-        ProfScope ps(MO_K_APPLY_X0, s, elems * (esz + (store_out ? esz : 8)));
-        if ((rc = checked(launch_apply_x0(a, chunk, s), s, "apply_x0"))) return rc;
-      } else {
-        const int T = tile_size(bin.cfg);
-        const int tm = bin.m_pad / T, tn = bin.n_pad / T;
-        const double m = bin.m, n = bin.n;
-        for (int k = 0; k < h.ns_steps; ++k) {
-          char* xrc = xr[k & 1];
-          char* xrn = xr[(k + 1) & 1];
-          const float* rs = k == 0 ? rscale : nullptr;
-          {  // S = X X^T
-            GemmArgs g{};
-            g.A = xrc; g.sA = L.x_elems;
-            g.B = xrc; g.sB = L.x_elems;
-            g.C = S;   g.sC = L.s_elems;
-            g.M = bin.m_pad; g.N = bin.m_pad; g.K = bin.n_pad;
-            g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tm * (tm + 1) / 2; g.batch = chunk;
-            g.rscale = rs; g.alpha = 1.0f; g.beta = 0.0f;
-            ProfScope ps(MO_K_GRAM, s, chunk * m * m * n);
-            if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_GRAM, g, s), s, "gram"))) return rc;
-          }
-          {  // P' = a I + b S + c S S
-            GemmArgs g{};
-            g.A = S; g.sA = L.s_elems;
-            g.B = S; g.sB = L.s_elems;
-            g.D = S; g.sD = L.s_elems;
-            g.C = P; g.sC = L.s_elems;
-            g.M = bin.m_pad; g.N = bin.m_pad; g.K = bin.m_pad;
-            g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tm * (tm + 1) / 2; g.batch = chunk;
-            g.rscale = nullptr; g.alpha = h.c; g.beta = h.b; g.gamma = h.a;
-            ProfScope ps(MO_K_POLY, s, chunk * m * m * m);
-            if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, EPI_POLY, g, s), s, "poly"))) return rc;
-          }
-          {  // X' = P' X, with X read K-major from its own layout
-            const bool last = (k + 1 == h.ns_steps);
-            GemmArgs g{};
-            g.A = P;   g.sA = L.s_elems;
-            g.B = xrc; g.sB = L.x_elems;
-            g.M = bin.m_pad; g.N = bin.n_pad; g.K = bin.m_pad;
-            g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn; g.batch = chunk;
-            g.rscale = rs;
-            Epi epi = EPI_UPDATE;
-            int cls = MO_K_UPDATE;
-            if (!last) {
-              g.C = xrn; g.sC = L.x_elems;
-            } else {
-              g.desc = desc;
-              g.m_true = bin.m; g.n_true = bin.n;
-              g.lrwd = lrwd; g.step = step;
-              g.rms_part = want_rms ? rms_part : nullptr;
-              if (store_out) {
-                epi = EPI_STORE;
-                g.out = static_cast<char*>(store_out) + static_cast<size_t>(c0) * store_stride * esz;
-                g.s_out = store_stride;
-              } else {
-                epi = EPI_APPLY;
-              }
-              cls = MO_K_APPLY;
-            }
-            ProfScope ps(cls, s, 2.0 * chunk * m * m * n);
-            if ((rc = checked(launch_gemm(plan.ns_dt, bin.cfg, epi, g, s), s, "update"))) return rc;
-          }
-        }
-      }
-      if (want_rms) {
-        RmsArgs a{};
-        a.desc = desc;
-        a.part = rms_part;
-        a.tiles = h.ns_steps == 0 ? L.x0_tiles : L.upd_tiles;
-        a.inv_count = 1.0 / (static_cast<double>(bin.m) * bin.n);
-        a.update_rms = update_rms;
-        ProfScope ps(MO_K_RMS, s, static_cast<double>(chunk) * a.tiles * 4);
-        if ((rc = checked(launch_rms(a, chunk, s), s, "rms"))) return rc;
-      }
+      std::vector<Item> items{make_item(bin, c0, std::min(cap, bin.count - c0))};
+      carve(items.back(), region, esz);
+      if ((rc = run_round(c, items))) return rc;
     }
   }
   return MO_OK;

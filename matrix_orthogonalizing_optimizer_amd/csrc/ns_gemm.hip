@@ -120,15 +120,6 @@ template <> struct Elem<float> {
   }
 };
 
-// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs.
-// Renumber so that each XCD owns one contiguous range of logical tiles and
-// neighbouring tiles (which share operand panels) meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  const int xcd = wg & 7, idx = wg >> 3;
-  const int q = total >> 3, r = total & 7;
-  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
 constexpr int kGroupM = 8;   // tile rows per group of the tile order
 
 // Tile order of a full tiles_m x tiles_n grid: groups of kGroupM tile rows,
@@ -240,25 +231,44 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   __shared__ u32x4 smem[kSmemChunks];
 
   const int tid = threadIdx.x;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = lid / p.tiles_per_mat;
-  const int t = lid - b * p.tiles_per_mat;
+  // Workgroup ids are dispatched round-robin over the 8 XCDs: this XCD's
+  // k-th workgroup takes the k-th tile of the XCD's share, walking the
+  // groups from group (xcd mod nbins) on; each group's share is a
+  // contiguous eighth of its tiles.
+  const int xcd = blockIdx.x & 7;
+  int k = blockIdx.x >> 3, bi = -1, lid = 0;
+  for (int jj = 0; jj < p.nbins; ++jj) {
+    const int bj = (xcd + jj) % p.nbins;
+    const int total = p.bin[bj].tiles_per_mat * p.bin[bj].batch;
+    const int q = total >> 3, r = total & 7;
+    const int cnt = q + (xcd < r ? 1 : 0);
+    if (k < cnt) {
+      bi = bj;
+      lid = xcd * q + min(xcd, r) + k;
+      break;
+    }
+    k -= cnt;
+  }
+  if (bi < 0) return;                           // this XCD has no more tiles
+  const GemmBin& g = p.bin[bi];
+  const int b = lid / g.tiles_per_mat;
+  const int t = lid - b * g.tiles_per_mat;
   int ti, tj;
-  if (kSym) sym_tile(t, p.tiles_m, ti, tj);
-  else grouped_tile(t, p.tiles_m, p.tiles_n, ti, tj);
+  if (kSym) sym_tile(t, g.tiles_m, ti, tj);
+  else grouped_tile(t, g.tiles_m, g.tiles_n, ti, tj);
 
   // row panels ti of A and tj of B: nk stages of TILE x BK each
-  const int nk = p.K / BK;
+  const int nk = g.K / BK;
   const int64_t stage_elems = static_cast<int64_t>(TILE) * BK;
-  const T* __restrict__ Ag = static_cast<const T*>(p.A) + b * p.sA + static_cast<int64_t>(ti) * nk * stage_elems;
-  const T* __restrict__ Bg = kNN ? static_cast<const T*>(p.B) + b * p.sB
-                                  : static_cast<const T*>(p.B) + b * p.sB + static_cast<int64_t>(tj) * nk * stage_elems;
+  const T* __restrict__ Ag = static_cast<const T*>(g.A) + b * g.sA + static_cast<int64_t>(ti) * nk * stage_elems;
+  const T* __restrict__ Bg = kNN ? static_cast<const T*>(g.B) + b * g.sB
+                                  : static_cast<const T*>(g.B) + b * g.sB + static_cast<int64_t>(tj) * nk * stage_elems;
   // K-major B: X is blocked [K / TILE panels][N / BK column stages][TILE][BK];
   // the 32 (bf16) or 16 (fp32) rows of stage kt in column stage c form one
   // contiguous block of BK rows x 64 bytes
   constexpr int kSPT = TILE / BK;                 // column stages per tile
   constexpr int kBlkBytes = BK * 64;              // bytes of one such block
-  const int nkb_b = p.N / BK;
+  const int nkb_b = g.N / BK;
   auto b_koff = [&](int kt) -> int64_t {          // elements: stage kt's row block
     const int pk = kt / kSPT, rr0 = (kt - pk * kSPT) * BK;
     return (static_cast<int64_t>(pk) * nkb_b * TILE + rr0) * BK;
@@ -431,13 +441,13 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // 32x32 accumulator layout: lane (l32, lh), register r holds
   // row 8*(r/4) + 4*lh + (r%4), column l32 of the block.
   float s = 1.0f;
-  if (p.rscale) {
-    s = p.rscale[b];
+  if (p.use_rscale) {
+    s = g.rscale[b];
     if (EPI == EPI_GRAM) s = s * s;
   }
-  const Blocked Lc = blocked(TILE, p.N, sizeof(T));       // C and D: [M, N]
-  T* __restrict__ C = static_cast<T*>(p.C) + b * p.sC;
-  const T* __restrict__ D = static_cast<const T*>(p.D) + (p.D ? b * p.sD : 0);
+  const Blocked Lc = blocked(TILE, g.N, sizeof(T));       // C and D: [M, N]
+  T* __restrict__ C = static_cast<T*>(g.C) + b * g.sC;
+  const T* __restrict__ D = static_cast<const T*>(g.D) + (g.D ? b * g.sD : 0);
 
   // Tile-local position (rr, cc) inside an LDS copy of one output tile,
   // which has the blocked layout of the tile's contiguous global range:
@@ -613,20 +623,20 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     // orientation; then every thread handles groups of four elements that
     // are consecutive along a parameter row: one 16-byte LDS read, one
     // 16-byte load and store of W.
-    const MatDesc md = p.desc[b];
+    const MatDesc md = g.desc[b];
     const bool ori = md.oriented != 0;
-    const int64_t ldw = ori ? p.m_true : p.n_true;         // parameter row length
-    const int wrows = ori ? p.n_true : p.m_true;            // parameter rows
-    const float lrwd = p.lrwd, stp = p.step;
+    const int64_t ldw = ori ? g.m_true : g.n_true;         // parameter row length
+    const int wrows = ori ? g.n_true : g.m_true;            // parameter rows
+    const float lrwd = p.lrwd, stp = g.step;
     // global address space: plain global loads and stores, not flat ones
     typedef __attribute__((address_space(1))) float gfloat;
     typedef __attribute__((address_space(1))) T gT;
     gfloat* __restrict__ W = (gfloat*)md.param;
-    gT* __restrict__ O = EPI == EPI_STORE ? (gT*)(static_cast<T*>(p.out) + b * p.s_out) : nullptr;
+    gT* __restrict__ O = EPI == EPI_STORE ? (gT*)(static_cast<T*>(g.out) + b * g.s_out) : nullptr;
     float* const lf = reinterpret_cast<float*>(smem);
     // padded LDS row lengths (consecutive lanes write consecutive rows)
     constexpr int kLd = TILE + 4, kLdT = kPR + 4;
-    const bool full = (ti + 1) * TILE <= p.m_true && (tj + 1) * TILE <= p.n_true && (ldw % 4) == 0;
+    const bool full = (ti + 1) * TILE <= g.m_true && (tj + 1) * TILE <= g.n_true && (ldw % 4) == 0;
     float sq = 0.0f;
     using True = std::integral_constant<bool, true>;
     using False = std::integral_constant<bool, false>;
@@ -742,7 +752,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     };
     if (ori) run(True{});
     else run(False{});
-    if (p.rms_part) {
+    if (g.rms_part) {
       // block reduction of the squared update (deterministic, no atomics)
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
@@ -751,7 +761,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       if (lane == 0) red[wave] = sq;
       __syncthreads();
       if (tid == 0)
-        p.rms_part[static_cast<int64_t>(b) * p.tiles_per_mat + t] =
+        g.rms_part[static_cast<int64_t>(b) * g.tiles_per_mat + t] =
             (red[0] + red[1]) + (red[2] + red[3]);
     }
   }
@@ -761,7 +771,7 @@ int tile_size(TileCfg t) { return t == TILE_256 ? 256 : (t == TILE_128 ? 128 : 6
 
 template <typename T, int TILE>
 static hipError_t launch_t(Epi epi, const GemmArgs& a, hipStream_t s) {
-  const int grid = a.tiles_per_mat * a.batch;
+  const int grid = 8 * a.per_xcd;
   switch (epi) {
     case EPI_GRAM:   hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_GRAM>), dim3(grid), dim3(256), 0, s, a); break;
     case EPI_POLY:   hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_POLY>), dim3(grid), dim3(256), 0, s, a); break;
