@@ -91,10 +91,12 @@ int mo_abi_version(void);
 const char* mo_last_error(void);
 
 /* Workspace needed by mo_muon_step for `tensors` with Newton-Schulz dtype
- * `ns_dtype`.  *full_bytes: enough to process every matrix of each shape
- * group in one pass (fastest).  *min_bytes (may be NULL): the smallest
- * workspace accepted; between the two, matrices of a shape group are
- * processed in several passes.  Host-only; touches no device state. */
+ * `ns_dtype`.  *full_bytes: every matrix of every shape group resident at
+ * once, so that each Newton-Schulz product is one launch over all groups
+ * (fastest).  *min_bytes (may be NULL): the smallest workspace accepted
+ * (one matrix at a time); between the two, shape groups are processed one
+ * after another, each in as few passes as fit.  Results do not depend on
+ * the workspace size.  Host-only; touches no device state. */
 int mo_muon_workspace_size(const mo_tensor* tensors, int64_t count,
                            int ns_dtype, size_t* full_bytes, size_t* min_bytes);
 
