@@ -79,10 +79,12 @@ struct GemmBin {
   int tiles_m, tiles_n, tiles_per_mat, batch;
   int m_true, n_true;
   float step;                            // EPI_APPLY: W <- W - (lrwd W + step x)
+  int super_order;                       // tiles in 16x16-tile super-blocks (see ns_gemm.hip)
 };
 struct GemmArgs {
   GemmBin bin[kMaxGroup];
   int nbins;
+  int rotate;                            // XCDs walk the groups in rotated order
   int per_xcd;                           // grid = 8 * per_xcd
   int use_rscale;                        // first iteration: scale by rscale
   float alpha, beta, gamma;              // EPI_POLY coefficients

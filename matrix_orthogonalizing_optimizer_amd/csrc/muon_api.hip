@@ -383,6 +383,7 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
     g.lrwd = c.lrwd;
     double work = 0.0;
     int per_xcd = 0;
+    bool all_super = true;
     const bool want_rms = c.update_rms != nullptr && c.store_out == nullptr;
     for (size_t j = i0; j < i1; ++j) {
       const Item& it = items[order[j]];
@@ -429,10 +430,15 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
         }
         work += 2.0 * it.chunk * m * m * n;
       }
+      const bool sym = (epi == EPI_GRAM || epi == EPI_POLY);
+      gb.super_order = (tm >= 16 && tm % 16 == 0 && (sym || tn % 16 == 0)) ? 1 : 0;
+      all_super = all_super && gb.super_order;
       const int total = gb.tiles_per_mat * gb.batch;
       per_xcd += (total + 7) / 8;
     }
     g.per_xcd = per_xcd;
+    // super-blocks need every XCD on the same block at a time
+    g.rotate = all_super ? 0 : 1;
     (void)N;
     ProfScope ps(cls, c.s, work);
     if ((rc = checked(launch_gemm(c.plan.ns_dt, cfg, epi, g, c.s), c.s, what))) return rc;

@@ -162,6 +162,46 @@ __device__ __forceinline__ void sym_tile(int t, int tiles_m, int& ti, int& tj) {
   ti = r0 + c + t;
 }
 
+// Super-block tile order for large matrices (tile counts multiples of 16).
+// The 256 tiles that run at once over the whole chip (8 XCDs x 32 CUs) form
+// one 16 x 16 block of tiles of one matrix; XCD x takes the 8 x 4 sub-block
+// at rows 8 (x % 2), columns 4 (x / 2).  The chip then streams 16 row and 16
+// column panels at a time instead of 12 per XCD, so what one XCD misses in
+// its L2 another has usually just brought into the chip-wide cache.
+// w: this XCD's tile index within the matrix; nsc: column super-blocks.
+__device__ __forceinline__ void super_gen(int w, int x, int nsc, int& ti, int& tj) {
+  const int sg = w >> 5, r = w & 31;
+  const int sr = sg / nsc, sc = sg - sr * nsc;
+  ti = sr * 16 + (x & 1) * 8 + (r & 7);
+  tj = sc * 16 + (x >> 1) * 4 + (r >> 3);
+}
+// Lower triangle of a square grid: super-blocks (sr, sc <= sr) in order;
+// an off-diagonal block gives each XCD its 8 x 4 sub-block (32 tiles), a
+// diagonal block (136 tiles) gives XCD x the lower parts of rows x and
+// 15 - x (17 tiles).
+__device__ __forceinline__ void super_sym(int w, int x, int& ti, int& tj) {
+  int sr = 0;
+  while (w >= 32 * sr + 17) {                    // tiles of super-row sr for one XCD
+    w -= 32 * sr + 17;
+    ++sr;
+  }
+  const int sc = w >> 5;
+  if (sc < sr) {
+    const int r = w & 31;
+    ti = sr * 16 + (x & 1) * 8 + (r & 7);
+    tj = sc * 16 + (x >> 1) * 4 + (r >> 3);
+  } else {
+    const int j = w - 32 * sr;                   // 0 .. 16
+    if (j <= x) {
+      ti = sr * 16 + x;
+      tj = sr * 16 + j;
+    } else {
+      ti = sr * 16 + 15 - x;
+      tj = sr * 16 + j - x - 1;
+    }
+  }
+}
+
 // Calls f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): the
 // indices are constants from the start, so small per-thread arrays indexed
 // by them are split into registers before any loop pass runs.
@@ -238,7 +278,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   const int xcd = blockIdx.x & 7;
   int k = blockIdx.x >> 3, bi = -1, lid = 0;
   for (int jj = 0; jj < p.nbins; ++jj) {
-    const int bj = (xcd + jj) % p.nbins;
+    const int bj = p.rotate ? (xcd + jj) % p.nbins : jj;
     const int total = p.bin[bj].tiles_per_mat * p.bin[bj].batch;
     const int q = total >> 3, r = total & 7;
     const int cnt = q + (xcd < r ? 1 : 0);
@@ -251,11 +291,26 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   }
   if (bi < 0) return;                           // this XCD has no more tiles
   const GemmBin& g = p.bin[bi];
-  const int b = lid / g.tiles_per_mat;
-  const int t = lid - b * g.tiles_per_mat;
-  int ti, tj;
-  if (kSym) sym_tile(t, g.tiles_m, ti, tj);
-  else grouped_tile(t, g.tiles_m, g.tiles_n, ti, tj);
+  int b, t, ti, tj;
+  if (g.super_order) {
+    // tiles_per_mat is a multiple of 8: every XCD runs tiles_per_mat / 8
+    // tiles of each matrix, matrices in order
+    const int per = g.tiles_per_mat >> 3;
+    b = k / per;
+    const int w = k - b * per;
+    if (kSym) {
+      super_sym(w, xcd, ti, tj);
+      t = ti * (ti + 1) / 2 + tj;
+    } else {
+      super_gen(w, xcd, g.tiles_n >> 4, ti, tj);
+      t = ti * g.tiles_n + tj;
+    }
+  } else {
+    b = lid / g.tiles_per_mat;
+    t = lid - b * g.tiles_per_mat;
+    if (kSym) sym_tile(t, g.tiles_m, ti, tj);
+    else grouped_tile(t, g.tiles_m, g.tiles_n, ti, tj);
+  }
 
   // row panels ti of A and tj of B: nk stages of TILE x BK each
   const int nk = g.K / BK;

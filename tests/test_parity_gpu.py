@@ -209,6 +209,24 @@ def test_step_bf16_mixed_shapes(mod, grad_dtype):
         print(MIXED[i], f"update rel_fro {e:.3e}")
 
 
+def test_step_super_block_order(mod, monkeypatch):
+    """64-wide tiles make these matrices 16 and 32 tiles a side, so the Gram,
+    polynomial, update and apply products run in the super-block tile order
+    used for large matrices, two shape groups per launch."""
+    monkeypatch.setenv("MO_TILE", "64")
+    shapes = [(1024, 1024), (1024, 2048), (2048, 1024)]
+    Ps, Gs, Ms = _mixed_state(700, shapes)
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    rms = torch.zeros(len(Ps), device=DEV)
+    mod.muon_step(Ps, Gs, Ms, update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    for i in range(len(Ps)):
+        e = _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), HYP)
+        print(shapes[i], f"update rel_fro {e:.3e}")
+
+
 @pytest.mark.parametrize("variant", [{"nesterov": False}, {"ns_steps": 0}, {"ns_steps": 1},
                                      {"ns_steps": 10}, {"mu": 0.0}])
 def test_step_variants(mod, variant):
