@@ -222,17 +222,22 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
 
 #define MO_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
 
-// One wave-wide direct-to-LDS load: lane l copies the 16 bytes at gptr
-// (its own address) to LDS byte address lds_base + 16 l.  Written as asm so
+// One wave-wide direct-to-LDS load: lane l copies the 16 bytes at
+// sbase + voff (its own address) to LDS byte address lds_base + 16 l.
+// sbase (a scalar 64-bit base) and lds_base must be wave-uniform; voff is the
+// lane's 32-bit byte offset, the same register for every load of a kernel,
+// so no address register is ever rewritten while a load that read it is in
+// flight.  (The instruction's immediate offset would move the LDS
+// destination as well as the source, so it stays 0.)  Written as asm so
 // that the compiler does not track these LDS writes: it would otherwise
 // drain every load in flight before each transposing LDS read it cannot
 // disambiguate.  The main loop orders them explicitly (s_waitcnt vmcnt
 // before each barrier, vmcnt(0) before LDS is reused).  The instruction
-// writes no registers; lds_base must be wave-uniform.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// writes no registers.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(lds_base)
+               : "v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -339,29 +344,28 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // wave-wide global_load_lds_dwordx4 copies 1 KiB of it (lane l moves the
   // 16 bytes at +16 l), and this wave's loads i cover 1 KiB pieces
   // wave*INST + i of the operand's block.
-  // The address of a load is a wave-uniform stage base (scalar registers)
-  // plus this lane's constant 32-bit byte offset, so no per-lane 64-bit
-  // arithmetic is repeated in the main loop.
-  const uint32_t lane_bytes = static_cast<uint32_t>((wave * INST * 64 + lane) * 16);
+  // The address of a load is a wave-uniform base (scalar registers) plus
+  // this lane's 16 l, so the main loop does no per-lane address arithmetic.
+  const uint32_t lane16 = static_cast<uint32_t>(lane * 16);
   // load q of this wave's DPW loads of stage kt into LDS buffer buf: even q
   // are pieces of A, odd q the matching pieces of B
   auto dma1 = [&](int buf, int kt, auto q) {
     constexpr int i = decltype(q)::value / 2;
     constexpr bool isB = decltype(q)::value % 2;
     u32x4* st = smem + buf * STAGE + (isB ? OPS : 0);
-    const char* src;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(st + (wave * INST + i) * 64));
     if constexpr (kNN && isB) {
       // piece wave*INST + i: 1 KiB of column stage (piece / (kBlkBytes / 1 KiB))
       const int piece = wave * INST + i;
       const int c = piece * 1024 / kBlkBytes, within = piece * 1024 - c * kBlkBytes;
       const char* base = reinterpret_cast<const char*>(
-          Bg + b_koff(kt) + static_cast<int64_t>(tj * kSPT + c) * TILE * BK);
-      src = base + (static_cast<uint32_t>(within) + static_cast<uint32_t>(lane * 16));
+          Bg + b_koff(kt) + static_cast<int64_t>(tj * kSPT + c) * TILE * BK) + within;
+      lds_dma16(base, lane16, lds);
     } else {
-      const char* base = reinterpret_cast<const char*>((isB ? Bg : Ag) + static_cast<int64_t>(kt) * stage_elems);
-      src = base + (lane_bytes + static_cast<uint32_t>(i * 1024));
+      const char* base = reinterpret_cast<const char*>((isB ? Bg : Ag) + static_cast<int64_t>(kt) * stage_elems) +
+                         (wave * INST + i) * 1024;
+      lds_dma16(base, lane16, lds);
     }
-    lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(st + (wave * INST + i) * 64)));
   };
   auto dma = [&](int buf, int kt) { unroll<DPW>([&](auto q) { dma1(buf, kt, q); }); };
 
