@@ -53,7 +53,9 @@ def measured_traffic(workload: str, epi: int = 2):
         return None
     n = b = 0.0
     for name, k in rec["kernels"].items():
-        if name.startswith("mo::ns_gemm_kernel") and name.endswith(f", {epi}>"):
+        # mo::ns_gemm_kernel<T, TILE, EPI, WAVES>
+        targs = name[name.find("<") + 1:name.rfind(">")].split(",")
+        if name.startswith("mo::ns_gemm_kernel") and len(targs) > 2 and int(targs[2]) == epi:
             n += k["dispatches"]
             b += k["dispatches"] * k["hbm_bytes_per_dispatch"]
     return b / n if n else None

@@ -139,7 +139,8 @@ int tile_size(TileCfg t);
 // Launchers (return hipError_t of the launch).
 hipError_t launch_prep(const PrepArgs& a, int chunk, hipStream_t s);
 hipError_t launch_norm(const NormArgs& a, int chunk, hipStream_t s);
-hipError_t launch_gemm(int ns_dt, TileCfg cfg, Epi epi, const GemmArgs& a,
+// waves: 4 (2 x 2 wave grid) or 8 (2 x 4; bf16 256-wide tiles only)
+hipError_t launch_gemm(int ns_dt, TileCfg cfg, Epi epi, int waves, const GemmArgs& a,
                        hipStream_t s);
 hipError_t launch_apply_x0(const ApplyX0Args& a, int chunk, hipStream_t s);
 hipError_t launch_rms(const RmsArgs& a, int chunk, hipStream_t s);

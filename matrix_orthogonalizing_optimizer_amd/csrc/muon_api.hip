@@ -361,6 +361,18 @@ float item_step(const StepCtx& c, const Item& it) {
   return static_cast<float>(static_cast<double>(c.h.lr) * scale);
 }
 
+// Waves per workgroup of a GEMM launch: bf16 256-wide tiles run 8 waves
+// (two per SIMD, so one wave's memory waits are covered by the other's
+// MFMAs; measured faster on every product), everything else 4.
+int gemm_waves(int ns_dt, TileCfg cfg) {
+  if (ns_dt != BF16 || cfg != TILE_256) return 4;
+  if (const char* e = std::getenv("MO_WAVES")) {
+    const int w = std::atoi(e);
+    if (w == 4 || w == 8) return w;
+  }
+  return 8;
+}
+
 // One Newton-Schulz product over a set of items: launches grouped by tile
 // configuration, up to kMaxGroup shape groups per launch.
 int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int cls, const char* what) {
@@ -441,7 +453,8 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
     g.rotate = all_super ? 0 : 1;
     (void)N;
     ProfScope ps(cls, c.s, work);
-    if ((rc = checked(launch_gemm(c.plan.ns_dt, cfg, epi, g, c.s), c.s, what))) return rc;
+    const int waves = gemm_waves(c.plan.ns_dt, cfg);
+    if ((rc = checked(launch_gemm(c.plan.ns_dt, cfg, epi, waves, g, c.s), c.s, what))) return rc;
     i0 = i1;
   }
   return MO_OK;

@@ -1,24 +1,26 @@
 // Newton-Schulz GEMMs on CDNA4 matrix cores (gfx950).
 //
 // Eq. 2 of "Muon is Scalable for LLM Training" (section 2.1) is evaluated as
-// three products per iteration, all of the form C = A * B^T with both
-// operands K-contiguous (row-major [rows, K]):
-//   Gram    S = X X^T                  A = B = X ([m, n])             symmetric
-//   Poly    P' = a I + b S + c S S^T   A = B = S (exactly symmetric)  symmetric
-//   Update  X' = P' X                  A = P', B = X^T ([n, m])
+// three products per iteration:
+//   Gram    S = X X^T                  A = B = X ([m, n], row panels)  symmetric
+//   Poly    P' = a I + b S + c S S^T   A = B = S (exactly symmetric)   symmetric
+//   Update  X' = P' X                  A = P', B = X read K-major
 // (a X + b S X + c S^2 X = (a I + b S + c S^2) X: the linear term rides in
-// P', whose diagonal is near 1 on converged directions.)
-// Keeping every iterate in both layouts (the Update epilogue writes X' and
-// X'^T) makes all three the same NT kernel.  The symmetric products compute
-// only lower-triangle tiles and write each tile twice (itself and its
-// mirror), so S and P are exactly symmetric.
+// P', whose diagonal is near 1 on converged directions.)  The last update
+// of a step is fused with the parameter update (apply) or with the output
+// store.  The symmetric products compute only lower-triangle tiles and
+// write each tile twice (itself and its mirror), so S and P are exactly
+// symmetric.
 //
-// Kernel shape: 256 threads = 4 waves in a 2x2 grid, square block tile of
-// TILE x TILE, K-steps of 128 bytes per row (64 bf16 / 32 fp32), operands
-// staged through LDS (double-buffered, 16-byte chunks XOR-swizzled by row),
-// wave tiles of (TILE/2)^2 built from 32x32 MFMA blocks:
+// Kernel shape: NW = 4 or 8 waves in a 2 x (NW / 2) grid over a square
+// TILE x TILE output tile; wave tiles of 32x32 MFMA blocks
 //   bf16: v_mfma_f32_32x32x16_bf16 (fp32 accumulate)
 //   fp32: v_mfma_f32_32x32x2_f32
+// K-steps of 64 bytes per row (32 bf16 / 16 fp32), operands copied straight
+// from global memory into a ring of LDS stages by direct-to-LDS loads, and
+// fragments read from LDS (transposing reads for the K-major operand) one
+// substep ahead of the MFMAs that use them.  With 8 waves two share each
+// SIMD, so one wave's memory waits are covered by the other's MFMAs.
 // All sizes are padded by the host to tile multiples (the padding is zero
 // and stays zero through the iteration), so the main loop has no bounds
 // checks; only the apply/store epilogues check against the true sizes.
@@ -26,8 +28,8 @@
 // Operands live in the blocked layout of mo_layout.h: one K-stage of one
 // row panel is a contiguous block that direct-to-LDS loads copy verbatim,
 // and an output tile is a contiguous range, so the Gram, polynomial and
-// update epilogues assemble the tile (and its mirror or transpose) in LDS
-// and stream it out with coalesced 16-byte stores.
+// update epilogues assemble the tile (and its mirror) in LDS and stream it
+// out with coalesced 16-byte stores.
 #include <utility>
 
 #include "mo_internal.h"
@@ -244,8 +246,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(MO_LDS(p)));
 }
 
-template <typename T, int TILE, int EPI>
-__global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
+template <typename T, int TILE, int EPI, int NW>
+__global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   using E = Elem<T>;
   constexpr bool kSym = (EPI == EPI_GRAM || EPI == EPI_POLY);
   // Products with X as the second factor (X' = P' X) read B = X in its own
@@ -258,21 +260,29 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   constexpr int kRowBytes = 64;                   // bytes of a tile row per stage
   constexpr int BK = kRowBytes / sizeof(T);       // K elements per stage
   constexpr int CPR = kRowBytes / 16;             // 16-byte chunks per row (4)
-  constexpr int NST = 4;                          // LDS stages (3 in flight)
-  constexpr int WT = TILE / 2;                    // wave tile edge
-  constexpr int FM = WT / 32;                     // 32x32 blocks per wave edge
+  // NW waves in a 2 x (NW / 2) grid; with 8 waves two share each SIMD and
+  // cover each other's waits, and three LDS stages (two in flight) suffice.
+  constexpr int NT = 64 * NW;                     // threads
+  constexpr int NST = NW == 8 ? 3 : 4;            // LDS stages
+  constexpr int WM = TILE / 2;                    // wave tile rows
+  constexpr int WN = TILE / (NW / 2);             // wave tile columns
+  constexpr int FMM = WM / 32, FMN = WN / 32;     // 32x32 blocks per wave tile
   constexpr int OPS = TILE * CPR;                 // chunks of one operand per stage
   constexpr int STAGE = 2 * OPS;                  // chunks per stage (A then B)
-  constexpr int RPI = 64 / CPR;                   // rows per wave-wide load (16)
-  constexpr int INST = TILE / RPI / 4;            // loads per wave per operand per stage
+  constexpr int INST = OPS / 64 / NW;             // 1 KiB loads per wave per operand per stage
   constexpr int DPW = 2 * INST;                   // loads per wave per stage
+  static_assert(INST >= 1 && OPS % (64 * NW) == 0, "stage split over the waves");
   // The apply/store epilogue stages the fp32 update through LDS in passes
   // of kPR tile rows, as [kPR][TILE + 4] (parameter rows = tile rows) or
   // [TILE][kPR + 4] (oriented parameters: parameter rows = tile columns).
   constexpr bool kApply = (EPI == EPI_APPLY || EPI == EPI_STORE);
   constexpr int kPR = TILE == 256 ? 128 : TILE;
   constexpr int kApplyFloats = TILE * (kPR + 4) > kPR * (TILE + 4) ? TILE * (kPR + 4) : kPR * (TILE + 4);
-  constexpr int kSmemChunks = (kApply && kApplyFloats / 4 > NST * STAGE) ? kApplyFloats / 4 : NST * STAGE;
+  // LDS: the main loop's stages, and what the epilogue stages -- the whole
+  // output tile (Gram, polynomial, update) or one apply pass
+  constexpr int kEpiChunks = kApply ? kApplyFloats / 4 : TILE * TILE * static_cast<int>(sizeof(T)) / 16;
+  constexpr int kSmemChunks = kEpiChunks > NST * STAGE ? kEpiChunks : NST * STAGE;
+  static_assert(kSmemChunks * 16 <= 160 * 1024, "LDS per workgroup");
   __shared__ u32x4 smem[kSmemChunks];
 
   const int tid = threadIdx.x;
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-  const int wr = (wave >> 1) * WT, wc = (wave & 1) * WT;
+  const int wr = (wave / (NW / 2)) * WM, wc = (wave % (NW / 2)) * WN;
   const int l32 = lane & 31, lh = lane >> 5;
 
   // Direct-to-LDS loads.  A stage of a panel is one contiguous block that
@@ -369,11 +379,11 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   };
   auto dma = [&](int buf, int kt) { unroll<DPW>([&](auto q) { dma1(buf, kt, q); }); };
 
-  f32x16_t acc[FM][FM];
+  f32x16_t acc[FMM][FMN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FMM; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FMN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
   // substep are read from LDS (set 0 / set 1 registers) while the MFMAs of
   // the other substep run.
   const int rsw = (l32 >> 2) & 3;               // slot swizzle of the rows this lane reads
-  u32x4 fa[2][FM], fb[2][FM];
+  u32x4 fa[2][FMM], fb[2][FMN];
   // B fragment of column block f from a K-major stage ([kSPT][BK rows][BK],
   // chunks permuted per row): this lane's column n = wc + 32 f + l32 and its
   // K values of substep ks.
@@ -416,13 +426,17 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     }
     return r;
   };
-  // fragment read q of substep ks into register set `set`: even q read A
-  // fragments, odd q B fragments
+  // fragment read q of substep ks into register set `set`: A and B
+  // fragments alternate (A0 B0 A1 B1 ...), the surplus of the longer side
+  // last, so the first MFMAs of the next substep have their operands early
+  constexpr int kPair = FMM < FMN ? FMM : FMN;
   auto frag1 = [&](int buf, auto ks, auto set, auto q) {
-    constexpr int f = decltype(q)::value / 2;
+    constexpr int Q = decltype(q)::value;
+    constexpr bool isA = Q < 2 * kPair ? (Q % 2 == 0) : (FMM > FMN);
+    constexpr int f = Q < 2 * kPair ? Q / 2 : Q - kPair;
     const u32x4* sA = smem + buf * STAGE;
     const int slot = (ks * 2 + lh) ^ rsw;
-    if constexpr (decltype(q)::value % 2 == 0) {
+    if constexpr (isA) {
       fa[set][f] = sA[(wr + f * 32 + l32) * CPR + slot];
     } else if constexpr (!kNN) {
       fb[set][f] = sA[OPS + (wc + f * 32 + l32) * CPR + slot];
@@ -430,8 +444,8 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       fb[set][f] = frag_kmajor(reinterpret_cast<const T*>(sA + OPS), ks, std::integral_constant<int, f>{});
     }
   };
-  constexpr int kGroups = FM * FM;              // MFMA groups (E::mma) per substep
-  constexpr int kReads = 2 * FM;                // fragment reads per substep
+  constexpr int kGroups = FMM * FMN;            // MFMA groups (E::mma) per substep
+  constexpr int kReads = FMM + FMN;             // fragment reads per substep
   // The MFMAs of one substep, each followed by its share of other work:
   // fragment reads rd(q) front-loaded (their results are needed by the
   // next substep), loads ld(q) spread evenly.  A scheduling fence after
@@ -441,10 +455,11 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     constexpr int kLd = std::decay_t<decltype(nld)>::value;
     unroll<kGroups>([&](auto g) {
       constexpr int G = decltype(g)::value;
+      constexpr int I = G / FMN, J = G % FMN;
       if constexpr (kNN)
-        acc[G / FM][G % FM] = E::mma(fb[set][G % FM], fa[set][G / FM], acc[G / FM][G % FM]);
+        acc[I][J] = E::mma(fb[set][J], fa[set][I], acc[I][J]);
       else
-        acc[G / FM][G % FM] = E::mma(fa[set][G / FM], fb[set][G % FM], acc[G / FM][G % FM]);
+        acc[I][J] = E::mma(fa[set][I], fb[set][J], acc[I][J]);
       constexpr int r0 = kReads <= kGroups ? G : G * kReads / kGroups;
       constexpr int r1 = kReads <= kGroups ? (G < kReads ? G + 1 : G) : (G + 1) * kReads / kGroups;
       unroll<r1 - r0>([&](auto k) { rd(std::integral_constant<int, r0 + decltype(k)::value>{}); });
@@ -516,18 +531,19 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     return (st * TILE + rr) * BK + ((ch ^ ((rr >> 2) & 3)) * E::kVec) + (c2 - ch * E::kVec);
   };
   T* const lt = reinterpret_cast<T*>(smem);                // TILE * TILE elements fit
+  static_assert(kApply || kSmemChunks * 16 >= TILE * TILE * static_cast<int>(sizeof(T)), "tile staging");
   constexpr int kTileChunks = TILE * TILE * static_cast<int>(sizeof(T)) / 16;
   // LDS tile -> contiguous global range: 16 bytes per thread and step, eight
   // steps' loads in flight before their stores
   auto copy_out = [&](T* dst) {
     u32x4* g = reinterpret_cast<u32x4*>(dst);
-    constexpr int kIter = kTileChunks / 256;
+    constexpr int kIter = kTileChunks / NT;
     constexpr int kB = kIter < 8 ? kIter : 8;
 #pragma unroll
     for (int c0 = 0; c0 < kIter; c0 += kB) {
       u32x4 v[kB];
-      unroll<kB>([&](auto k) { v[decltype(k)::value] = smem[tid + (c0 + decltype(k)::value) * 256]; });
-      unroll<kB>([&](auto k) { g[tid + (c0 + decltype(k)::value) * 256] = v[decltype(k)::value]; });
+      unroll<kB>([&](auto k) { v[decltype(k)::value] = smem[tid + (c0 + decltype(k)::value) * NT]; });
+      unroll<kB>([&](auto k) { g[tid + (c0 + decltype(k)::value) * NT] = v[decltype(k)::value]; });
     }
   };
 
@@ -538,8 +554,8 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     // store into the LDS copy of the tile, then one coalesced copy-out.
     int on[4];
     unroll<4>([&](auto q) { on[q] = loff(wr + l32, wc + 8 * q + 4 * lh); });
-    unroll<FM>([&](auto i) {
-      unroll<FM>([&](auto j) {
+    unroll<FMM>([&](auto i) {
+      unroll<FMN>([&](auto j) {
         unroll<4>([&](auto q) {
           constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
           const int o = on[Q] + 32 * I * BK + (32 * J / BK) * TILE * BK;
@@ -580,15 +596,15 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       // element (rr, cc) of this tile is (cc, rr) there, so each lane reads
       // its four consecutive rows with one access
       const u32x4* dsrc = reinterpret_cast<const u32x4*>(D + blk_tile(Lc, tj, ti));
-      for (int c = tid; c < kTileChunks; c += 256) {
+      for (int c = tid; c < kTileChunks; c += NT) {
         const int wave_base = c - lane;                  // uniform across the wave
         __builtin_amdgcn_global_load_lds(static_cast<void*>(const_cast<u32x4*>(dsrc + c)),
                                          MO_LDS(smem + wave_base), 16, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       barrier();
-      unroll<FM>([&](auto i) {
-        unroll<FM>([&](auto j) {
+      unroll<FMM>([&](auto i) {
+        unroll<FMN>([&](auto j) {
           unroll<4>([&](auto q) {
             constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
             float d[4];
@@ -600,20 +616,25 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
           });
         });
       });
-      if (diag && wr == wc) {
-        unroll<FM>([&](auto i) {
-          constexpr int I = decltype(i)::value;
-          unroll<16>([&](auto r) {
-            constexpr int R = decltype(r)::value;
-            if (l32 == 8 * (R / 4) + 4 * lh + (R % 4)) acc[I][I][R] += p.gamma;
+      if (diag) {
+        // a I on the blocks that straddle the diagonal
+        unroll<FMM>([&](auto i) {
+          unroll<FMN>([&](auto j) {
+            constexpr int I = decltype(i)::value, J = decltype(j)::value;
+            if (wr + 32 * I == wc + 32 * J) {
+              unroll<16>([&](auto r) {
+                constexpr int R = decltype(r)::value;
+                if (l32 == 8 * (R / 4) + 4 * lh + (R % 4)) acc[I][J][R] += p.gamma;
+              });
+            }
           });
         });
       }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       barrier();                                  // the S tile is no longer needed
     } else {
-      unroll<FM>([&](auto i) {
-        unroll<FM>([&](auto j) {
+      unroll<FMM>([&](auto i) {
+        unroll<FMN>([&](auto j) {
           unroll<16>([&](auto r) {
             acc[decltype(i)::value][decltype(j)::value][decltype(r)::value] *= s;
           });
@@ -626,8 +647,8 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     // puts every value at its mirror position and the direct pass below
     // then overwrites the lower triangle, leaving the tile exactly
     // symmetric.
-    unroll<FM>([&](auto i) {
-      unroll<FM>([&](auto j) {
+    unroll<FMM>([&](auto i) {
+      unroll<FMN>([&](auto j) {
         unroll<4>([&](auto q) {
           constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
           E::store4(lt + toff(i, j, q), acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
@@ -661,10 +682,10 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       });
     };
     if (!diag) {
-      unroll<FM>([&](auto i) { unroll<FM>([&](auto j) { direct_block(i, j, false); }); });
+      unroll<FMM>([&](auto i) { unroll<FMN>([&](auto j) { direct_block(i, j, false); }); });
     } else {
-      unroll<FM>([&](auto i) {
-        unroll<FM>([&](auto j) {
+      unroll<FMM>([&](auto i) {
+        unroll<FMN>([&](auto j) {
           const int br = wr + 32 * decltype(i)::value, bc = wc + 32 * decltype(j)::value;
           if (br > bc) direct_block(i, j, false);
           else if (br == bc) direct_block(i, j, true);
@@ -706,8 +727,8 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       constexpr int pass = decltype(pc)::value;
       constexpr bool kOri = decltype(oric)::value;
       const int r_base = wr - pass * kPR;
-      unroll<FM>([&](auto i) {
-        unroll<FM>([&](auto j) {
+      unroll<FMM>([&](auto i) {
+        unroll<FMN>([&](auto j) {
           unroll<4>([&](auto q) {
             constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
             const int rr = r_base + 32 * I + l32;
@@ -743,21 +764,21 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       }
     };
     constexpr int kGroups = kPR * TILE / 4;                 // groups per pass
-    constexpr int kU = kGroups >= 256 * 8 ? 8 : kGroups / 256;
-    static_assert(kGroups % (256 * kU) == 0, "group loop");
+    constexpr int kU = kGroups >= NT * 8 ? 8 : kGroups / NT;
+    static_assert(kU >= 1 && kGroups % (NT * kU) == 0, "group loop");
     // whole tile inside the parameter, rows a multiple of 4: all of a step's
     // loads (LDS x, W) are issued before any store
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(1))) f32x4_t gf4;
     auto copy_full = [&](auto pc, auto oric) {
 #pragma unroll 1
-      for (int g0 = 0; g0 < kGroups; g0 += 256 * kU) {
+      for (int g0 = 0; g0 < kGroups; g0 += NT * kU) {
         f32x4_t xv[kU], wv[kU];
         int64_t off[kU];
         unroll<kU>([&](auto u) {
           constexpr int U = decltype(u)::value;
           int wrow, wcol;
-          const int lo = group(pc, oric, g0 + U * 256 + tid, wrow, wcol);
+          const int lo = group(pc, oric, g0 + U * NT + tid, wrow, wcol);
           off[U] = static_cast<int64_t>(wrow) * ldw + wcol;
           xv[U] = *reinterpret_cast<const f32x4_t*>(lf + lo);
           if constexpr (EPI == EPI_APPLY) wv[U] = *(const gf4*)(W + off[U]);
@@ -778,7 +799,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
     // ragged tile or row length not a multiple of 4: element by element
     auto copy_edge = [&](auto pc, auto oric) {
 #pragma unroll 1
-      for (int g = tid; g < kGroups; g += 256) {
+      for (int g = tid; g < kGroups; g += NT) {
         int wrow, wcol;
         const int lo = group(pc, oric, g, wrow, wcol);
         if (wrow >= wrows) continue;
@@ -819,40 +840,43 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(GemmArgs p) {
       float* red = reinterpret_cast<float*>(smem);
       if (lane == 0) red[wave] = sq;
       __syncthreads();
-      if (tid == 0)
-        g.rms_part[static_cast<int64_t>(b) * g.tiles_per_mat + t] =
-            (red[0] + red[1]) + (red[2] + red[3]);
+      if (tid == 0) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += red[w];
+        g.rms_part[static_cast<int64_t>(b) * g.tiles_per_mat + t] = tot;
+      }
     }
   }
 }
 
 int tile_size(TileCfg t) { return t == TILE_256 ? 256 : (t == TILE_128 ? 128 : 64); }
 
-template <typename T, int TILE>
+template <typename T, int TILE, int NW>
 static hipError_t launch_t(Epi epi, const GemmArgs& a, hipStream_t s) {
-  const int grid = 8 * a.per_xcd;
+  const dim3 grid(8 * a.per_xcd), block(64 * NW);
   switch (epi) {
-    case EPI_GRAM:   hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_GRAM>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_POLY:   hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_POLY>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_UPDATE: hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_UPDATE>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_APPLY:  hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_APPLY>), dim3(grid), dim3(256), 0, s, a); break;
-    case EPI_STORE:  hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_STORE>), dim3(grid), dim3(256), 0, s, a); break;
+    case EPI_GRAM:   hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_GRAM, NW>), grid, block, 0, s, a); break;
+    case EPI_POLY:   hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_POLY, NW>), grid, block, 0, s, a); break;
+    case EPI_UPDATE: hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_UPDATE, NW>), grid, block, 0, s, a); break;
+    case EPI_APPLY:  hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_APPLY, NW>), grid, block, 0, s, a); break;
+    case EPI_STORE:  hipLaunchKernelGGL((ns_gemm_kernel<T, TILE, EPI_STORE, NW>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int ns_dt, TileCfg cfg, Epi epi, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(int ns_dt, TileCfg cfg, Epi epi, int waves, const GemmArgs& a, hipStream_t s) {
   if (ns_dt == BF16) {
     switch (cfg) {
-      case TILE_256: return launch_t<uint16_t, 256>(epi, a, s);
-      case TILE_128: return launch_t<uint16_t, 128>(epi, a, s);
-      case TILE_64:  return launch_t<uint16_t, 64>(epi, a, s);
+      case TILE_256: return waves == 8 ? launch_t<uint16_t, 256, 8>(epi, a, s) : launch_t<uint16_t, 256, 4>(epi, a, s);
+      case TILE_128: return launch_t<uint16_t, 128, 4>(epi, a, s);
+      case TILE_64:  return launch_t<uint16_t, 64, 4>(epi, a, s);
     }
   } else {
     switch (cfg) {
       case TILE_256: return hipErrorInvalidValue;   // fp32 tiles stop at 128
-      case TILE_128: return launch_t<float, 128>(epi, a, s);
-      case TILE_64:  return launch_t<float, 64>(epi, a, s);
+      case TILE_128: return launch_t<float, 128, 4>(epi, a, s);
+      case TILE_64:  return launch_t<float, 64, 4>(epi, a, s);
     }
   }
   return hipErrorInvalidValue;

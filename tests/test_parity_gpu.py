@@ -227,6 +227,38 @@ def test_step_super_block_order(mod, monkeypatch):
         print(shapes[i], f"update rel_fro {e:.3e}")
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_step_tile256_waves(mod, monkeypatch, waves):
+    """256-wide tiles with 4 or 8 waves per workgroup on every product
+    (Gram, polynomial, update, apply), on shapes with ragged edges, both
+    orientations and diagonal tiles that straddle several waves."""
+    monkeypatch.setenv("MO_TILE", "256")
+    monkeypatch.setenv("MO_WAVES", waves)
+    shapes = [(300, 700), (700, 300), (512, 1024), (257, 1031), (1031, 257), (64, 600)]
+    Ps, Gs, Ms = _mixed_state(800, shapes)
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    rms = torch.zeros(len(Ps), device=DEV)
+    mod.muon_step(Ps, Gs, Ms, update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    for i in range(len(Ps)):
+        e = _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), HYP)
+        print(shapes[i], waves, f"update rel_fro {e:.3e}")
+
+
+def test_ns_store_tile256_waves8(mod, monkeypatch):
+    """The store epilogue (orthogonalize only) with 8 waves."""
+    monkeypatch.setenv("MO_TILE", "256")
+    monkeypatch.setenv("MO_WAVES", "8")
+    for shape in [(300, 700), (700, 300)]:
+        x = randn(shape, 17 + shape[0], dtype=torch.bfloat16)
+        X = mod.newton_schulz(x, ns_steps=5)
+        torch.cuda.synchronize()
+        ref, _ = mo.orthogonalize(f64(x), 5, eps=1e-7)
+        assert sp.rel_fro(f64(X), ref) <= 2e-2
+
+
 @pytest.mark.parametrize("variant", [{"nesterov": False}, {"ns_steps": 0}, {"ns_steps": 1},
                                      {"ns_steps": 10}, {"mu": 0.0}])
 def test_step_variants(mod, variant):
