@@ -363,9 +363,12 @@ float item_step(const StepCtx& c, const Item& it) {
 
 // Waves per workgroup of a GEMM launch: bf16 256-wide tiles run 8 waves
 // (two per SIMD, so one wave's memory waits are covered by the other's
-// MFMAs; measured faster on every product), everything else 4.
-int gemm_waves(int ns_dt, TileCfg cfg) {
+// MFMAs; measured faster on every product), everything else 4.  The 8-wave
+// polynomial product folds b S into the accumulators as (b / c) S, so a
+// polynomial without the S^2 term (c = 0) runs 4 waves.
+int gemm_waves(int ns_dt, TileCfg cfg, Epi epi, float c) {
   if (ns_dt != BF16 || cfg != TILE_256) return 4;
+  if (epi == EPI_POLY && c == 0.0f) return 4;
   if (const char* e = std::getenv("MO_WAVES")) {
     const int w = std::atoi(e);
     if (w == 4 || w == 8) return w;
@@ -453,7 +456,7 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
     g.rotate = all_super ? 0 : 1;
     (void)N;
     ProfScope ps(cls, c.s, work);
-    const int waves = gemm_waves(c.plan.ns_dt, cfg);
+    const int waves = gemm_waves(c.plan.ns_dt, cfg, epi, g.alpha);
     if ((rc = checked(launch_gemm(c.plan.ns_dt, cfg, epi, waves, g, c.s), c.s, what))) return rc;
     i0 = i1;
   }

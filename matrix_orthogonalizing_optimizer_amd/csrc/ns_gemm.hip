@@ -242,6 +242,12 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
                : "v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
+// x of lane l ^ 32 (the other half of the wave), without LDS.
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(MO_LDS(p)));
 }
@@ -479,6 +485,45 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   using LD = std::integral_constant<int, DPW>;
   auto no_ld = [](auto) {};
 
+  // Polynomial product, bf16: the epilogue's b S term is taken from the B
+  // operand while it streams through.  The tile's S[rows ti, cols tj] equals
+  // S[cols tj, rows ti] (S is exactly symmetric), and that block is the B
+  // panel (rows tj) at the K-stages of tile ti's columns: the stage of
+  // accumulator row block i is kSPT ti + wr / 32 + i.  In the B fragment of
+  // column block j a lane (l32, lh) holds S[row wc + 32 j + l32 of panel tj]
+  // at K offsets 16 ks + 8 lh + 0..7; accumulator registers 4 q + e need the
+  // K offsets 8 q + 4 lh + e: for q = 2 ks + lh the lane's own elements
+  // 4 lh .. 4 lh + 3, for the other q the same elements of lane l ^ 32.
+  // They are added as (b / c) S, so that the epilogue's c acc gives
+  // c S S + b S.  This is the 8-wave bf16 kernel's only path (the host runs
+  // c = 0 with 4 waves); the others read S in the epilogue.
+  constexpr bool kCapture = (EPI == EPI_POLY) && sizeof(T) == 2 && NW == 8;
+  constexpr bool cap = kCapture;
+  const float bc = cap ? p.beta / p.alpha : 0.0f;
+  const int cap_kt = kCapture ? (TILE / BK) * ti + wr / BK : 0;
+  // adds (b / c) S for accumulator row block I from register set `set`
+  // (substep ks of the stage cap_kt + I)
+  auto capture = [&](auto i, auto set, auto ks) {
+    constexpr int I = decltype(i)::value, KS = decltype(ks)::value;
+    unroll<FMN>([&](auto j) {
+      constexpr int J = decltype(j)::value;
+      const u32x4 f = fb[set][J];
+      const uint32_t own0 = lh ? f[2] : f[0], own1 = lh ? f[3] : f[1];
+      const uint32_t oth0 = lane_xor32(lh ? f[0] : f[2]), oth1 = lane_xor32(lh ? f[1] : f[3]);
+      const uint32_t a0 = lh ? oth0 : own0, a1 = lh ? oth1 : own1;   // q = 2 ks
+      const uint32_t b0 = lh ? own0 : oth0, b1 = lh ? own1 : oth1;   // q = 2 ks + 1
+      constexpr int R = 8 * KS;
+      acc[I][J][R + 0] += bc * __uint_as_float(a0 << 16);
+      acc[I][J][R + 1] += bc * __uint_as_float(a0 & 0xffff0000u);
+      acc[I][J][R + 2] += bc * __uint_as_float(a1 << 16);
+      acc[I][J][R + 3] += bc * __uint_as_float(a1 & 0xffff0000u);
+      acc[I][J][R + 4] += bc * __uint_as_float(b0 << 16);
+      acc[I][J][R + 5] += bc * __uint_as_float(b0 & 0xffff0000u);
+      acc[I][J][R + 6] += bc * __uint_as_float(b1 << 16);
+      acc[I][J][R + 7] += bc * __uint_as_float(b1 & 0xffff0000u);
+    });
+  };
+
   // Main loop.  Stage kt lives in LDS buffer kt % NST.  Every iteration
   // issues exactly one stage of loads (stage kt + NST, or -- past the end
   // -- the last stage again into the buffer that has just been consumed),
@@ -494,9 +539,13 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   barrier();
   unroll<kReads>([&](auto q) { frag1(0, S0{}, S0{}, q); });
   __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // one stage: substep 0, wait + barrier, substep 1 with the next stage's
+  // loads; capI >= 0 adds the captured b S of row block capI (see above)
+  auto iteration = [&](int kt, auto capi) {
+    constexpr int CI = decltype(capi)::value;
     const int cur = kt % NST;
     pipelined(S0{}, L0{}, [&](auto q) { frag1(cur, S1{}, S1{}, q); }, no_ld);
+    if constexpr (CI >= 0) capture(capi, S0{}, S0{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * DPW));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
@@ -504,6 +553,17 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     const int kl = min(kt + NST, nk - 1);
     pipelined(S1{}, LD{}, [&](auto q) { frag1(nxt, S0{}, S0{}, q); },
               [&](auto q) { dma1(cur, kl, q); });
+    if constexpr (CI >= 0) capture(capi, S1{}, S1{});
+  };
+  using NoCap = std::integral_constant<int, -1>;
+  if constexpr (!cap) {
+    for (int kt = 0; kt < nk; ++kt) iteration(kt, NoCap{});
+  } else {
+    // the FMM capture stages unrolled, so every accumulator index is a
+    // compile-time constant
+    for (int kt = 0; kt < cap_kt; ++kt) iteration(kt, NoCap{});
+    unroll<FMM>([&](auto i) { iteration(cap_kt + decltype(i)::value, i); });
+    for (int kt = cap_kt + FMM; kt < nk; ++kt) iteration(kt, NoCap{});
   }
   // every load has landed and every wave is done with the staged tiles
   // before LDS is reused
@@ -592,30 +652,41 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     const bool diag = kSym && (ti == tj);
 
     if constexpr (EPI == EPI_POLY) {
-      // b S + a I from the mirror tile S[tj, ti] (S is exactly symmetric):
-      // element (rr, cc) of this tile is (cc, rr) there, so each lane reads
-      // its four consecutive rows with one access
-      const u32x4* dsrc = reinterpret_cast<const u32x4*>(D + blk_tile(Lc, tj, ti));
-      for (int c = tid; c < kTileChunks; c += NT) {
-        const int wave_base = c - lane;                  // uniform across the wave
-        __builtin_amdgcn_global_load_lds(static_cast<void*>(const_cast<u32x4*>(dsrc + c)),
-                                         MO_LDS(smem + wave_base), 16, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      barrier();
-      unroll<FMM>([&](auto i) {
-        unroll<FMN>([&](auto j) {
-          unroll<4>([&](auto q) {
-            constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
-            float d[4];
-            E::load4(lt + toff(i, j, q), d);
-            unroll<4>([&](auto e) {
-              constexpr int R = 4 * Q + decltype(e)::value;
-              acc[I][J][R] = p.alpha * acc[I][J][R] + p.beta * d[decltype(e)::value];
+      if constexpr (cap) {
+        // b S is already in the accumulators (captured in the main loop)
+        unroll<FMM>([&](auto i) {
+          unroll<FMN>([&](auto j) {
+            unroll<16>([&](auto r) {
+              acc[decltype(i)::value][decltype(j)::value][decltype(r)::value] *= p.alpha;
             });
           });
         });
-      });
+      } else {
+        // b S + a I from the mirror tile S[tj, ti] (S is exactly symmetric):
+        // element (rr, cc) of this tile is (cc, rr) there, so each lane reads
+        // its four consecutive rows with one access
+        const u32x4* dsrc = reinterpret_cast<const u32x4*>(D + blk_tile(Lc, tj, ti));
+        for (int c = tid; c < kTileChunks; c += NT) {
+          const int wave_base = c - lane;                  // uniform across the wave
+          __builtin_amdgcn_global_load_lds(static_cast<void*>(const_cast<u32x4*>(dsrc + c)),
+                                           MO_LDS(smem + wave_base), 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        barrier();
+        unroll<FMM>([&](auto i) {
+          unroll<FMN>([&](auto j) {
+            unroll<4>([&](auto q) {
+              constexpr int I = decltype(i)::value, J = decltype(j)::value, Q = decltype(q)::value;
+              float d[4];
+              E::load4(lt + toff(i, j, q), d);
+              unroll<4>([&](auto e) {
+                constexpr int R = 4 * Q + decltype(e)::value;
+                acc[I][J][R] = p.alpha * acc[I][J][R] + p.beta * d[decltype(e)::value];
+              });
+            });
+          });
+        });
+      }
       if (diag) {
         // a I on the blocks that straddle the diagonal
         unroll<FMM>([&](auto i) {

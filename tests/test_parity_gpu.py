@@ -259,6 +259,23 @@ def test_ns_store_tile256_waves8(mod, monkeypatch):
         assert sp.rel_fro(f64(X), ref) <= 2e-2
 
 
+@pytest.mark.parametrize("abc", [(1.5, -0.5, 0.0), (3.0, -3.2, 1.2)])
+def test_ns_custom_coeffs_tile256(mod, monkeypatch, abc):
+    """Other polynomial coefficients on 256-wide tiles: without the quintic
+    term (c = 0, which takes the 4-wave polynomial product that reads S in
+    its epilogue) and with a different b / c ratio (8 waves, b S folded into
+    the accumulators)."""
+    monkeypatch.setenv("MO_TILE", "256")
+    for shape in [(300, 700), (512, 512)]:
+        x = randn(shape, 23 + shape[1], dtype=torch.bfloat16)
+        X = mod.newton_schulz(x, ns_steps=5, abc=abc)
+        torch.cuda.synchronize()
+        ref, _ = mo.orthogonalize(f64(x), 5, abc=abc, eps=1e-7)
+        err = sp.rel_fro(f64(X), ref)
+        print(shape, abc, f"rel_fro {err:.3e}")
+        assert err <= 2e-2
+
+
 @pytest.mark.parametrize("variant", [{"nesterov": False}, {"ns_steps": 0}, {"ns_steps": 1},
                                      {"ns_steps": 10}, {"mu": 0.0}])
 def test_step_variants(mod, variant):
