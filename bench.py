@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--workload", default="dense800m",
                     help="dense800m (default), llama1p5b_gqa, moe_share, large_n5, "
                          "large_n10, fp32_128x512")
+    ap.add_argument("--scaling", default="shape", choices=["shape", "hidden", "update_norm"],
+                    help="update scaling: 0.2 sqrt(max(A,B)) (default), 0.2 sqrt(H) with H the "
+                         "largest matrix dimension, or 0.2 / RMS(X_N)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not bracket launches with HIP events")
@@ -145,9 +148,11 @@ def main():
 
     step_no = [0]
 
+    hidden = float(max(max(g.rows, g.cols) for g in wl.mats))
+
     def opt_step():
         step_no[0] += 1
-        plan.step(ns_steps=wl.ns_steps, workspace=ws, **HYPER)
+        plan.step(ns_steps=wl.ns_steps, workspace=ws, scaling=args.scaling, hidden=hidden, **HYPER)
         if A is not None:
             mo_amd.adamw_step(A.params, A.grads, A.m, A.v, lr=HYPER["lr"], wd=HYPER["wd"],
                               step=step_no[0])
@@ -200,7 +205,8 @@ def main():
         "data": "synthetic (seeded; random-init weights, Gaussian gradients)",
         "config": {"workload": wl.key, "muon_matrices": wl.n_mats,
                    "muon_elements": wl.n_elems, "adamw_elements": wl.n_vec_elems,
-                   "ns_steps": wl.ns_steps, "grad_dtype": str(wl.grad_dtype).split(".")[-1],
+                   "ns_steps": wl.ns_steps, "scaling": args.scaling,
+                   "grad_dtype": str(wl.grad_dtype).split(".")[-1],
                    "mom_dtype": str(wl.mom_dtype).split(".")[-1]},
         "matrices_per_s": wl.n_mats * steps_per_s,
         "ns_alg_tflop_per_step": alg_flops / 1e12,

@@ -13,7 +13,9 @@
  *     decay and the shape scale 0.2 * sqrt(max(A, B));
  *   - section 2.2 (matching AdamW's update RMS): RMSNorm, embedding and LM
  *     head parameters use AdamW with the same learning rate and decay;
- *   - section 2.3, Algorithm 1: the per-matrix update RMS is reported.
+ *   - section 2.3, Algorithm 1: the per-matrix update RMS is reported;
+ *   - section 3.1, Eq. 5 and Eq. 6: the alternative update scalings
+ *     0.2 * sqrt(H) and 0.2 / RMS(O) (mo_muon_plan_set_scaling).
  *
  * General rules for every entry point
  *   Memory   All tensor pointers are DEVICE pointers on the current HIP
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MO_ABI_VERSION 1
+#define MO_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum mo_status {
@@ -150,6 +152,30 @@ int mo_muon_plan_step(mo_muon_plan* plan, float lr, float wd, float mu,
                       int nesterov, int ns_steps, const float* abc,
                       float rms_scale, float eps, float* update_rms,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* How X_N (= O_t) is scaled in the update (section 3.1):
+ *   MO_SCALE_SHAPE        Eq. 4 / Eq. 7: rms_scale * sqrt(max(rows, cols)),
+ *                         the default of every step entry point;
+ *   MO_SCALE_HIDDEN       Eq. 5: rms_scale * sqrt(H) for one model-wide H
+ *                         (the hidden size), whatever the matrix shape;
+ *   MO_SCALE_UPDATE_NORM  Eq. 6: rms_scale / RMS(X_N), RMS over the
+ *                         rows * cols elements, so the update term has RMS
+ *                         exactly rms_scale; a matrix whose X_N is zero gets
+ *                         a decay-only update.  X_N's RMS is computed on the
+ *                         device from the fp32 values before the apply (one
+ *                         extra pass of the last Newton-Schulz product). */
+typedef enum mo_scaling {
+    MO_SCALE_SHAPE = 0,
+    MO_SCALE_HIDDEN = 1,
+    MO_SCALE_UPDATE_NORM = 2
+} mo_scaling;
+
+/* Sets the scaling used by the plan's later mo_muon_plan_step calls
+ * (initially MO_SCALE_SHAPE).  hidden: H for MO_SCALE_HIDDEN (finite,
+ * >= 1), ignored otherwise.  Host-only.  With MO_SCALE_UPDATE_NORM,
+ * update_rms receives RMS(X_N) as with the other scalings.
+ * Returns MO_OK or MO_EINVAL (plan unchanged). */
+int mo_muon_plan_set_scaling(mo_muon_plan* plan, int scaling, float hidden);
 
 /* Frees the plan's descriptor table (synchronises the device first). */
 int mo_muon_plan_destroy(mo_muon_plan* plan);

@@ -147,6 +147,9 @@ def muon_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                              _stream_handle(dev, stream)))
 
 
+_SCALINGS = {"shape": 0, "hidden": 1, "update_norm": 2}
+
+
 class MuonPlan:
     """``mo_muon_plan_*``: binds one list of matrices for repeated steps."""
 
@@ -173,9 +176,18 @@ class MuonPlan:
     def step(self, *, lr: float, wd: float = 0.1, mu: float = 0.95, nesterov: bool = True,
              ns_steps: int = 5, abc=None, rms_scale: float = 0.2, eps: float = 1e-7,
              update_rms: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+             workspace: Optional[torch.Tensor] = None, stream=None,
+             scaling: str = "shape", hidden: Optional[float] = None) -> None:
+        """scaling: "shape" (0.2 sqrt(max(A, B)), Eq. 4 / 7), "hidden"
+        (0.2 sqrt(hidden), Eq. 5) or "update_norm" (0.2 / RMS(X_N), Eq. 6)."""
         if self._h is None:
             raise RuntimeError("plan was closed")
+        if scaling not in _SCALINGS:
+            raise ValueError(f"scaling must be one of {sorted(_SCALINGS)}")
+        if scaling == "hidden" and hidden is None:
+            raise ValueError('scaling="hidden" needs hidden=H')
+        check(lib().mo_muon_plan_set_scaling(self._h, _SCALINGS[scaling],
+                                             float(hidden) if hidden is not None else 0.0))
         if workspace is None:
             workspace = _workspace(self.device, self.workspace_bytes)
         check(lib().mo_muon_plan_step(self._h, lr, wd, mu, int(nesterov), ns_steps, _abc(abc),

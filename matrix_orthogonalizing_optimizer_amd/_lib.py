@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmuon.so")
 
 MO_OK, MO_EINVAL, MO_EUNSUPPORTED, MO_EWORKSPACE, MO_EHIP = 0, -1, -2, -3, -4
 MO_F32, MO_BF16 = 0, 1
+MO_SCALE_SHAPE, MO_SCALE_HIDDEN, MO_SCALE_UPDATE_NORM = 0, 1, 2
 (MO_K_MOMENTUM, MO_K_NORM, MO_K_GRAM, MO_K_POLY, MO_K_UPDATE, MO_K_APPLY,
  MO_K_APPLY_X0, MO_K_RMS, MO_K_ADAMW) = range(9)
 KERNEL_CLASS_NAMES = ["momentum", "norm", "gram", "poly", "update", "apply",
@@ -55,6 +56,7 @@ _SIGS = {
     "mo_muon_plan_step": (_c.c_int, [_P, _c.c_float, _c.c_float, _c.c_float, _c.c_int, _c.c_int,
                                      _c.POINTER(_c.c_float), _c.c_float, _c.c_float,
                                      _P, _P, _c.c_size_t, _P]),
+    "mo_muon_plan_set_scaling": (_c.c_int, [_P, _c.c_int, _c.c_float]),
     "mo_muon_plan_destroy": (_c.c_int, [_P]),
     "mo_adamw_step": (_c.c_int, [_c.POINTER(MoTensor), _c.c_int64, _c.c_int, _c.c_float,
                                  _c.c_float, _c.c_double, _c.c_double, _c.c_float, _c.c_int64, _P]),

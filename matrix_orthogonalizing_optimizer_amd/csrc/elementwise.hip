@@ -202,6 +202,7 @@ __global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
   const Blocked Lx = blocked(p.tile, p.n_pad, esz);
   const float r0 = p.rscale[b];
   const float lrwd = p.lrwd;
+  const float stp = p.step_dev ? p.step_dev[b] : p.step;
   const int c = tb * 64 + tx * 4;
   const int nvalid = max(0, min(4, B - c));
   const bool vec = ((B & 3) == 0) && nvalid == 4;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(256) void apply_x0_kernel(ApplyX0Args p) {
       float w[4];
       load4(md.param, F32, off, nvalid, vec, w);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = w[j] - (lrwd * w[j] + p.step * x[j]);
+      for (int j = 0; j < 4; ++j) w[j] = w[j] - (lrwd * w[j] + stp * x[j]);
       store4(md.param, F32, off, nvalid, vec, w);
     }
   }
@@ -250,7 +251,15 @@ __global__ __launch_bounds__(64) void rms_kernel(RmsArgs p) {
   for (int i = threadIdx.x; i < p.tiles; i += 64) s += static_cast<double>(part[i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (threadIdx.x == 0) p.update_rms[p.desc[b].out_index] = static_cast<float>(sqrt(s * p.inv_count));
+  if (threadIdx.x == 0) {
+    if (p.rscale) {
+      const double r = static_cast<double>(p.rscale[b]);
+      s *= r * r;
+    }
+    const double rms = sqrt(s * p.inv_count);
+    if (p.update_rms) p.update_rms[p.desc[b].out_index] = static_cast<float>(rms);
+    if (p.step) p.step[b] = rms > 0.0 ? static_cast<float>(static_cast<double>(p.lr_scale) / rms) : 0.0f;
+  }
 }
 
 // AdamW: each block covers kAdamElemsPerBlock consecutive elements of one

@@ -79,6 +79,7 @@ struct GemmBin {
   int tiles_m, tiles_n, tiles_per_mat, batch;
   int m_true, n_true;
   float step;                            // EPI_APPLY: W <- W - (lrwd W + step x)
+  const float* step_dev;                 // EPI_APPLY: per batch entry step (replaces step) or null
   int super_order;                       // tiles in 16x16-tile super-blocks (see ns_gemm.hip)
 };
 struct GemmArgs {
@@ -89,6 +90,7 @@ struct GemmArgs {
   int use_rscale;                        // first iteration: scale by rscale
   float alpha, beta, gamma;              // EPI_POLY coefficients
   float lrwd;                            // EPI_APPLY
+  int rms_only;                          // EPI_APPLY: only write the rms_part partials of x
 };
 
 // Elementwise apply for ns_steps = 0 (X_N = X_0), and for EPI_STORE with 0
@@ -102,17 +104,24 @@ struct ApplyX0Args {
   int tiles_per_mat;                     // 64x64 tiles of the true domain
   const float* rscale;
   float lrwd, step;
+  const float* step_dev;                 // per matrix step (replaces step) or null
   int ns_dt;
   void* out; int64_t s_out;              // store mode when non-null
   float* rms_part;                       // [chunk][tiles_per_mat] or null
 };
 
+// Per matrix: rms = sqrt(sum(part) * mult * inv_count) with mult = rscale^2
+// (partials of N, ns_steps = 0) or 1 (partials of X_N); writes rms to
+// update_rms[out_index] and/or step = lr_scale / rms (0 when rms = 0).
 struct RmsArgs {
   const MatDesc* desc;
   const float* part;
   int tiles;
   double inv_count;      // 1 / (rows * cols)
-  float* update_rms;     // indexed by desc[i].out_index
+  float* update_rms;     // indexed by desc[i].out_index, or null
+  const float* rscale;   // mult = rscale[i]^2 when non-null
+  float* step;           // [chunk] or null
+  float lr_scale;        // lr * rms_scale
 };
 
 constexpr int kAdamMaxTensors = 32;

@@ -252,6 +252,7 @@ int build_plan(const mo_tensor* t, int64_t count, int grad_dt, int mom_dt, int n
 
 // Workspace layout ---------------------------------------------------------
 // [descriptor table (one-shot calls only)] [rscale: count floats]
+// [step: count floats (update-norm scaling)]
 // then, reused by every bin in turn, for a chunk of `cap` matrices:
 // [norm partials] [rms partials] [X][X'][S][P]
 struct BinLayout {
@@ -274,7 +275,7 @@ BinLayout bin_layout(const Bin& b, int esz) {
 size_t fixed_bytes(const HostPlan& p, bool with_table) {
   size_t f = 0;
   if (with_table) f += align_up(p.descs.size() * sizeof(MatDesc));
-  f += align_up(static_cast<size_t>(p.count) * 4);
+  f += 2 * align_up(static_cast<size_t>(p.count) * 4);
   return f;
 }
 
@@ -303,6 +304,8 @@ struct Hyper {
   float lr, wd, mu, a, b, c, rms_scale, eps;
   int nesterov, ns_steps;
   bool has_mom;
+  int scaling;      // MO_SCALE_*
+  float hidden;     // H of MO_SCALE_HIDDEN
 };
 
 int validate_hyper(const Hyper& h) {
@@ -322,6 +325,7 @@ struct Item {
   int c0, chunk;
   const MatDesc* desc;
   float* rscale;
+  float* step;        // per matrix step of the update-norm scaling
   float* norm_part;
   float* rms_part;
   char* x[2];
@@ -356,8 +360,13 @@ struct StepCtx {
   float lrwd;
 };
 
+// lr times the scale of X_N in the update: Eq. 4 / Eq. 7 rms_scale
+// sqrt(max(A, B)), or Eq. 5 rms_scale sqrt(H).  (Eq. 6 scales per matrix on
+// the device: Item::step.)
 float item_step(const StepCtx& c, const Item& it) {
-  const double scale = static_cast<double>(c.h.rms_scale) * std::sqrt(static_cast<double>(it.bin->n));
+  const double root = c.h.scaling == MO_SCALE_HIDDEN ? std::sqrt(static_cast<double>(c.h.hidden))
+                                                     : std::sqrt(static_cast<double>(it.bin->n));
+  const double scale = static_cast<double>(c.h.rms_scale) * root;
   return static_cast<float>(static_cast<double>(c.h.lr) * scale);
 }
 
@@ -378,7 +387,10 @@ int gemm_waves(int ns_dt, TileCfg cfg, Epi epi, float c) {
 
 // One Newton-Schulz product over a set of items: launches grouped by tile
 // configuration, up to kMaxGroup shape groups per launch.
-int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int cls, const char* what) {
+// rms_only (EPI_APPLY): the scale pass of the update-norm scaling, which
+// only writes the partial sums of squares of X_N.
+int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int cls, const char* what,
+               bool rms_only = false) {
   int rc;
   const int N = c.h.ns_steps;
   std::vector<int> order(items.size());
@@ -396,6 +408,8 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
     g.use_rscale = (k == 0 && (epi == EPI_GRAM || epi == EPI_UPDATE || epi == EPI_APPLY || epi == EPI_STORE)) ? 1 : 0;
     g.alpha = c.h.c; g.beta = c.h.b; g.gamma = c.h.a;
     g.lrwd = c.lrwd;
+    g.rms_only = rms_only ? 1 : 0;
+    const bool unorm = c.h.scaling == MO_SCALE_UPDATE_NORM && c.store_out == nullptr;
     double work = 0.0;
     int per_xcd = 0;
     bool all_super = true;
@@ -437,13 +451,14 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
           gb.desc = it.desc;
           gb.m_true = bin.m; gb.n_true = bin.n;
           gb.step = item_step(c, it);
-          gb.rms_part = want_rms ? it.rms_part : nullptr;
+          gb.step_dev = unorm ? it.step : nullptr;
+          gb.rms_part = rms_only ? it.rms_part : (want_rms && !unorm ? it.rms_part : nullptr);
           if (epi == EPI_STORE) {
             gb.out = static_cast<char*>(c.store_out) + static_cast<size_t>(it.c0) * c.store_stride * c.esz;
             gb.s_out = c.store_stride;
           }
         }
-        work += 2.0 * it.chunk * m * m * n;
+        if (!rms_only) work += 2.0 * it.chunk * m * m * n;
       }
       const bool sym = (epi == EPI_GRAM || epi == EPI_POLY);
       gb.super_order = (tm >= 16 && tm % 16 == 0 && (sym || tn % 16 == 0)) ? 1 : 0;
@@ -494,8 +509,25 @@ int run_round(const StepCtx& c, std::vector<Item>& items) {
     ProfScope ps(MO_K_NORM, c.s, static_cast<double>(it.chunk) * it.L.prep_tiles * 4);
     if ((rc = checked(launch_norm(na, it.chunk, c.s), c.s, "norm"))) return rc;
   }
+  // Eq. 6 (update-norm scaling): the per-matrix step lr rms_scale / RMS(X_N)
+  // is computed on the device before the apply; it also yields update_rms
+  const bool unorm = h.scaling == MO_SCALE_UPDATE_NORM && c.store_out == nullptr;
+  auto scale_pass = [&](Item& it, const float* part, int tiles, const float* rscale) {
+    RmsArgs a{};
+    a.desc = it.desc;
+    a.part = part;
+    a.tiles = tiles;
+    a.inv_count = 1.0 / (static_cast<double>(it.bin->m) * it.bin->n);
+    a.update_rms = want_rms ? c.update_rms : nullptr;
+    a.rscale = rscale;
+    a.step = it.step;
+    a.lr_scale = static_cast<float>(static_cast<double>(h.lr) * h.rms_scale);
+    ProfScope ps(MO_K_RMS, c.s, static_cast<double>(it.chunk) * tiles * 4);
+    return checked(launch_rms(a, it.chunk, c.s), c.s, "scale");
+  };
   if (h.ns_steps == 0) {
     for (Item& it : items) {
+      if (unorm && (rc = scale_pass(it, it.norm_part, it.L.prep_tiles, it.rscale))) return rc;
       const Bin& bin = *it.bin;
       ApplyX0Args a{};
       a.desc = it.desc;
@@ -507,11 +539,12 @@ int run_round(const StepCtx& c, std::vector<Item>& items) {
       a.rscale = it.rscale;
       a.lrwd = c.lrwd;
       a.step = item_step(c, it);
+      a.step_dev = unorm ? it.step : nullptr;
       a.ns_dt = plan.ns_dt;
       a.out = c.store_out ? static_cast<char*>(c.store_out) + static_cast<size_t>(it.c0) * c.store_stride * c.esz
                           : nullptr;
       a.s_out = c.store_stride;
-      a.rms_part = want_rms ? it.rms_part : nullptr;
+      a.rms_part = want_rms && !unorm ? it.rms_part : nullptr;
       const double elems = static_cast<double>(it.chunk) * bin.m * bin.n;
       ProfScope ps(MO_K_APPLY_X0, c.s, elems * (c.esz + (c.store_out ? c.esz : 8)));
       if ((rc = checked(launch_apply_x0(a, it.chunk, c.s), c.s, "apply_x0"))) return rc;
@@ -522,10 +555,15 @@ int run_round(const StepCtx& c, std::vector<Item>& items) {
       if ((rc = gemm_phase(c, items, EPI_GRAM, k, MO_K_GRAM, "gram"))) return rc;
       if ((rc = gemm_phase(c, items, EPI_POLY, k, MO_K_POLY, "poly"))) return rc;
       const Epi ue = !last ? EPI_UPDATE : (c.store_out ? EPI_STORE : EPI_APPLY);
+      if (last && unorm) {
+        if ((rc = gemm_phase(c, items, EPI_APPLY, k, MO_K_UPDATE, "update norm", true))) return rc;
+        for (Item& it : items)
+          if ((rc = scale_pass(it, it.rms_part, it.L.upd_tiles, nullptr))) return rc;
+      }
       if ((rc = gemm_phase(c, items, ue, k, last ? MO_K_APPLY : MO_K_UPDATE, "update"))) return rc;
     }
   }
-  if (want_rms) {
+  if (want_rms && !unorm) {
     for (Item& it : items) {
       RmsArgs a{};
       a.desc = it.desc;
@@ -549,7 +587,8 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
              size_t ws_bytes, size_t fixed_used, hipStream_t s, void* store_out, int64_t store_stride) {
   const int esz = plan.esz();
   float* rscale_all = reinterpret_cast<float*>(ws + fixed_used);
-  char* region = ws + fixed_used + align_up(static_cast<size_t>(plan.count) * 4);
+  float* step_all = reinterpret_cast<float*>(ws + fixed_used + align_up(static_cast<size_t>(plan.count) * 4));
+  char* region = ws + fixed_used + 2 * align_up(static_cast<size_t>(plan.count) * 4);
   const size_t region_bytes = ws_bytes - static_cast<size_t>(region - ws);
   StepCtx c{plan, h, update_rms, s, store_out, store_stride, esz,
             static_cast<float>(static_cast<double>(h.lr) * h.wd)};
@@ -561,6 +600,7 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
     it.chunk = chunk;
     it.desc = d_desc + bin.first + c0;
     it.rscale = rscale_all + bin.first + c0;
+    it.step = step_all + bin.first + c0;
     return it;
   };
   size_t all = 0;
@@ -643,6 +683,7 @@ Hyper make_hyper(float lr, float wd, float mu, int nesterov, int ns_steps, const
   h.b = abc ? abc[1] : -4.7750f;
   h.c = abc ? abc[2] : 2.0315f;
   h.rms_scale = rms_scale; h.eps = eps; h.has_mom = has_mom;
+  h.scaling = MO_SCALE_SHAPE; h.hidden = 0.0f;
   return h;
 }
 
@@ -652,6 +693,8 @@ struct mo_muon_plan {
   HostPlan plan;
   MatDesc* d_desc = nullptr;
   int device = 0;
+  int scaling = MO_SCALE_SHAPE;
+  float hidden = 0.0f;
 };
 
 extern "C" {
@@ -732,7 +775,9 @@ int mo_muon_plan_step(mo_muon_plan* plan, float lr, float wd, float mu, int nest
                       const float* abc, float rms_scale, float eps, float* update_rms, void* workspace,
                       size_t workspace_bytes, void* stream) {
   if (!plan) return fail(MO_EINVAL, "plan is NULL");
-  const Hyper h = make_hyper(lr, wd, mu, nesterov, ns_steps, abc, rms_scale, eps, true);
+  Hyper h = make_hyper(lr, wd, mu, nesterov, ns_steps, abc, rms_scale, eps, true);
+  h.scaling = plan->scaling;
+  h.hidden = plan->hidden;
   int rc;
   if ((rc = validate_hyper(h))) return rc;
   if (update_rms && (reinterpret_cast<uintptr_t>(update_rms) & 3u))
@@ -746,6 +791,18 @@ int mo_muon_plan_step(mo_muon_plan* plan, float lr, float wd, float mu, int nest
     return fail(MO_EINVAL, "plan was created on device %d, current device is %d", plan->device, dev);
   return run_step(plan->plan, plan->d_desc, h, update_rms, static_cast<char*>(workspace), workspace_bytes, 0,
                   static_cast<hipStream_t>(stream), nullptr, 0);
+}
+
+int mo_muon_plan_set_scaling(mo_muon_plan* plan, int scaling, float hidden) {
+  if (!plan) return fail(MO_EINVAL, "plan is NULL");
+  if (scaling != MO_SCALE_SHAPE && scaling != MO_SCALE_HIDDEN && scaling != MO_SCALE_UPDATE_NORM)
+    return fail(MO_EINVAL, "scaling must be MO_SCALE_SHAPE, MO_SCALE_HIDDEN or MO_SCALE_UPDATE_NORM (got %d)",
+                scaling);
+  if (scaling == MO_SCALE_HIDDEN && !(finite(hidden) && hidden >= 1.0f))
+    return fail(MO_EINVAL, "hidden must be finite and >= 1 for MO_SCALE_HIDDEN");
+  plan->scaling = scaling;
+  plan->hidden = scaling == MO_SCALE_HIDDEN ? hidden : 0.0f;
+  return MO_OK;
 }
 
 int mo_muon_plan_destroy(mo_muon_plan* plan) {

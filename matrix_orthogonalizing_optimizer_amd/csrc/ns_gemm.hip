@@ -774,11 +774,38 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     // orientation; then every thread handles groups of four elements that
     // are consecutive along a parameter row: one 16-byte LDS read, one
     // 16-byte load and store of W.
+    if constexpr (EPI == EPI_APPLY) {
+      if (p.rms_only) {
+        // sum of squares of x = s acc only (the scale pass of the
+        // update-norm scaling); padded rows and columns hold exact zeros
+        float sq = 0.0f;
+        unroll<FMM>([&](auto i) {
+          unroll<FMN>([&](auto j) {
+            unroll<16>([&](auto r) {
+              const float x = s * acc[decltype(i)::value][decltype(j)::value][decltype(r)::value];
+              sq += x * x;
+            });
+          });
+        });
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        float* red = reinterpret_cast<float*>(smem);
+        if (lane == 0) red[wave] = sq;
+        __syncthreads();
+        if (tid == 0) {
+          float tot = 0.0f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) tot += red[w];
+          g.rms_part[static_cast<int64_t>(b) * g.tiles_per_mat + t] = tot;
+        }
+        return;
+      }
+    }
     const MatDesc md = g.desc[b];
     const bool ori = md.oriented != 0;
     const int64_t ldw = ori ? g.m_true : g.n_true;         // parameter row length
     const int wrows = ori ? g.n_true : g.m_true;            // parameter rows
-    const float lrwd = p.lrwd, stp = g.step;
+    const float lrwd = p.lrwd, stp = g.step_dev ? g.step_dev[b] : g.step;
     // global address space: plain global loads and stores, not flat ones
     typedef __attribute__((address_space(1))) float gfloat;
     typedef __attribute__((address_space(1))) T gT;

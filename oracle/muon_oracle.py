@@ -23,6 +23,8 @@ the Traditional-Chinese translation page of the technical report):
 * section 2.2, "other hyper-parameters" -- N = 5 and mu = 0.95;
 * section 2.3, Algorithm 1 -- the step reports ``sqrt(mean(u^2))`` of the
   update for logging;
+* section 3.1, Eq. 5 and Eq. 6 -- the alternative update scalings
+  ``0.2 * sqrt(H)`` (H the model's hidden size) and ``0.2 / RMS(O_t)``;
 * section 2.2 (matching AdamW's update RMS) -- RMSNorm, embedding and LM head
   parameters use AdamW with the same learning rate and weight decay.
 
@@ -36,6 +38,8 @@ design notes of the repository):
   odd matrix polynomial this is exact in real arithmetic; it keeps the Gram
   matrix on the short side;
 * the reported RMS is that of the unscaled Newton-Schulz output ``X_N``;
+* Eq. 6 with ``O_t = 0`` (zero gradient history): ``O_t / RMS(O_t)`` is
+  taken as zero, so the step is decay only (the same as the other scalings);
 * AdamW's beta1, beta2, eps and bias correction are not printed on the pages
   (they only say "standard AdamW"): the defaults of the cited Adam paper
   (0.9, 0.999, 1e-8, with bias correction) are used, and the decay is applied
@@ -123,16 +127,32 @@ def shape_scale(rows: int, cols: int, rms_scale: float = RMS_SCALE) -> float:
     return rms_scale * math.sqrt(max(rows, cols))
 
 
-def apply_update(W, X_N, lr: float, wd: float, rms_scale: float = RMS_SCALE):
-    """Section 2.2, Eq. 4 (= section 3.1, Eq. 7).
+def apply_update(W, X_N, lr: float, wd: float, rms_scale: float = RMS_SCALE,
+                 scaling: str = "shape", hidden=None):
+    """The scaled, decoupled-decay update of one matrix.
 
-    ``W_t = W_{t-1} - lr * (0.2 * X_N * sqrt(max(A, B)) + wd * W_{t-1})``:
-    the decay term uses the weights from before this step.
+    scaling "shape": section 2.2, Eq. 4 (= section 3.1, Eq. 7),
+        ``W_t = W_{t-1} - lr * (0.2 * X_N * sqrt(max(A, B)) + wd * W_{t-1})``;
+    scaling "hidden": section 3.1, Eq. 5, ``0.2 * X_N * sqrt(H)`` in place of
+        the shape factor (``hidden`` = H);
+    scaling "update_norm": section 3.1, Eq. 6, ``0.2 * X_N / RMS(X_N)``.
+    The decay term uses the weights from before this step.
     """
     W = _f64(W)
     X_N = _f64(X_N)
     rows, cols = W.shape
-    return W - lr * (shape_scale(rows, cols, rms_scale) * X_N + wd * W)
+    if scaling == "shape":
+        U = shape_scale(rows, cols, rms_scale) * X_N
+    elif scaling == "hidden":
+        if hidden is None:
+            raise ValueError("scaling 'hidden' needs H")
+        U = rms_scale * math.sqrt(hidden) * X_N
+    elif scaling == "update_norm":
+        r = update_rms(X_N)
+        U = rms_scale * X_N / r if r > 0.0 else np.zeros_like(X_N)
+    else:
+        raise ValueError(f"unknown scaling {scaling!r}")
+    return W - lr * (U + wd * W)
 
 
 def update_rms(X_N) -> float:
@@ -144,17 +164,19 @@ def update_rms(X_N) -> float:
 
 def muon_step(W, G, M, *, lr: float, wd: float, mu: float = MOMENTUM,
               nesterov: bool = True, ns_steps: int = NS_STEPS, abc=NS_COEFFS,
-              rms_scale: float = RMS_SCALE, eps: float = NORM_EPS):
+              rms_scale: float = RMS_SCALE, eps: float = NORM_EPS,
+              scaling: str = "shape", hidden=None):
     """One Muon step for one matrix parameter ``W [A, B]``.
 
     Momentum (Eq. 1 + Nesterov), Frobenius normalisation and Newton-Schulz
-    (Eq. 2), then the scaled, decoupled-decay update (Eq. 4).
+    (Eq. 2), then the scaled, decoupled-decay update (Eq. 4; Eq. 5 or Eq. 6
+    with ``scaling``).
 
     Returns ``(W_new, M_new, X_N, rms_of_X_N)``.
     """
     M_new, N = momentum_update(M, G, mu, nesterov)
     X_N, _ = orthogonalize(N, ns_steps, abc, eps)
-    W_new = apply_update(W, X_N, lr, wd, rms_scale)
+    W_new = apply_update(W, X_N, lr, wd, rms_scale, scaling, hidden)
     return W_new, M_new, X_N, update_rms(X_N)
 
 

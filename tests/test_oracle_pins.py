@@ -238,6 +238,64 @@ def test_update_rms_of_full_step(m, n):
     assert abs(rms - fx / math.sqrt(n)) < 1e-13
 
 
+# ---------------------------------------------------------------- Eq. 5 / Eq. 6 scalings
+
+@pytest.mark.parametrize("shape", [(64, 256), (256, 64), (50, 50)])
+def test_eq5_hidden_scale(shape):
+    """Section 3.1, Eq. 5: with H = max(A, B) it is Eq. 4 exactly; with the
+    exact polar factor (Lemma 1: RMS 1/sqrt(max(A, B))) the update RMS is
+    0.2 sqrt(H / max(A, B)) for any H."""
+    r = _rng(5 + shape[0] + shape[1])
+    W = r.normal(0, 0.02, shape)
+    O = sp.polar_factor(r.standard_normal(shape))
+    lr, wd = 1e-3, 0.1
+    a = mo.apply_update(W, O, lr, wd, scaling="hidden", hidden=max(shape))
+    b = mo.apply_update(W, O, lr, wd)
+    assert np.array_equal(a, b)
+    for H in (128, 1536, 7):
+        W1 = mo.apply_update(W, O, lr, wd, scaling="hidden", hidden=H)
+        upd = (W - W1) / lr - wd * W
+        assert abs(math.sqrt(np.mean(upd ** 2)) - 0.2 * math.sqrt(H / max(shape))) < 1e-10
+
+
+@pytest.mark.parametrize("shape,rank", [((64, 256), 64), ((256, 64), 20), ((40, 40), 3), ((1, 300), 1)])
+def test_eq6_update_norm_rms_is_0p2(shape, rank):
+    """Section 3.1, Eq. 6: the update term 0.2 O / RMS(O) has RMS exactly
+    0.2 whatever O is (any rank, any scale), and O and t O give the same
+    step for t > 0."""
+    r = _rng(11 + rank)
+    U, _ = np.linalg.qr(r.standard_normal((shape[0], rank)))
+    V, _ = np.linalg.qr(r.standard_normal((shape[1], rank)))
+    O = U @ np.diag(r.uniform(0.1, 2.0, rank)) @ V.T
+    W = r.normal(0, 0.02, shape)
+    lr, wd = 1e-3, 0.1
+    W1 = mo.apply_update(W, O, lr, wd, scaling="update_norm")
+    upd = (W - W1) / lr - wd * W
+    assert abs(math.sqrt(np.mean(upd ** 2)) - 0.2) < 1e-12
+    W2 = mo.apply_update(W, 7.25 * O, lr, wd, scaling="update_norm")
+    assert np.allclose(W1, W2, rtol=0, atol=1e-15)
+
+
+def test_eq6_zero_update_is_decay_only():
+    W = _rng(3).normal(0, 0.02, (8, 12))
+    W1 = mo.apply_update(W, np.zeros_like(W), 1e-3, 0.1, scaling="update_norm")
+    assert np.array_equal(W1, W - 1e-3 * (0.1 * W))
+
+
+def test_eq6_full_step_rms():
+    """Through the whole step: whatever N does to the singular values, the
+    update-norm step moves W by exactly lr * 0.2 in RMS (plus the decay)."""
+    r = _rng(41)
+    W = r.normal(0, 0.02, (48, 96))
+    G = r.normal(0, 1e-3, (48, 96))
+    M = r.normal(0, 1e-3, (48, 96))
+    for steps in (0, 1, 5):
+        W1, _, X, rms = mo.muon_step(W, G, M, **dict(HYPER, ns_steps=steps), scaling="update_norm")
+        upd = (W - W1) / HYPER["lr"] - HYPER["wd"] * W
+        assert abs(math.sqrt(np.mean(upd ** 2)) - 0.2) < 1e-12
+        assert abs(rms - math.sqrt(np.mean(X ** 2))) < 1e-15
+
+
 # ---------------------------------------------------------------- momentum
 
 def test_momentum_closed_form():
@@ -388,3 +446,42 @@ def test_mutants_are_caught():
     assert _pins_fail(_mk_step(apply=apply_sqrt_min), _mk_orth(mo.newton_schulz))
     assert _pins_fail(_mk_step(apply=apply_decay_after), _mk_orth(mo.newton_schulz))
     assert _pins_fail(_mk_step(apply=apply_no_scale), _mk_orth(mo.newton_schulz))
+
+
+def _scaling_pins_fail(apply_fn):
+    """The Eq. 5 / Eq. 6 pins above, run on a candidate apply_update."""
+    r = _rng(77)
+    fails = []
+    W = r.normal(0, 0.02, (32, 96))
+    O = sp.polar_factor(r.standard_normal((32, 96)))
+    lr, wd = 1e-3, 0.1
+    W1 = apply_fn(W, O, lr, wd, 0.2, "hidden", 300)
+    upd = (W - W1) / lr - wd * W
+    fails.append(abs(math.sqrt(np.mean(upd ** 2)) - 0.2 * math.sqrt(300 / 96)) > 1e-10)
+    O2 = O[:, :] * np.linspace(0.2, 1.5, 96)[None, :]
+    W1 = apply_fn(W, O2, lr, wd, 0.2, "update_norm", None)
+    upd = (W - W1) / lr - wd * W
+    fails.append(abs(math.sqrt(np.mean(upd ** 2)) - 0.2) > 1e-12)
+    return any(fails)
+
+
+def test_scaling_mutants_are_caught():
+    assert not _scaling_pins_fail(mo.apply_update)
+
+    def hidden_uses_shape(W, X, lr, wd, s, scaling, hidden):
+        if scaling == "hidden":
+            return mo.apply_update(W, X, lr, wd, s)
+        return mo.apply_update(W, X, lr, wd, s, scaling, hidden)
+
+    def norm_by_frobenius(W, X, lr, wd, s, scaling, hidden):   # ||O||_F instead of RMS(O)
+        if scaling == "update_norm":
+            return W - lr * (s * X / np.linalg.norm(X) + wd * W)
+        return mo.apply_update(W, X, lr, wd, s, scaling, hidden)
+
+    def norm_times_shape(W, X, lr, wd, s, scaling, hidden):    # Eq. 6 and Eq. 4 combined
+        if scaling == "update_norm":
+            return W - lr * (s * math.sqrt(max(W.shape)) * X / mo.update_rms(X) + wd * W)
+        return mo.apply_update(W, X, lr, wd, s, scaling, hidden)
+
+    for fn in (hidden_uses_shape, norm_by_frobenius, norm_times_shape):
+        assert _scaling_pins_fail(fn), fn.__name__

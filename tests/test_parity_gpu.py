@@ -276,6 +276,56 @@ def test_ns_custom_coeffs_tile256(mod, monkeypatch, abc):
         assert err <= 2e-2
 
 
+@pytest.mark.parametrize("scaling", ["hidden", "update_norm"])
+@pytest.mark.parametrize("ns_steps", [0, 1, 5])
+@pytest.mark.parametrize("tile", [None, "256"])
+def test_step_alternative_scalings(mod, monkeypatch, scaling, ns_steps, tile):
+    """Section 3.1's Eq. 5 (0.2 sqrt(H)) and Eq. 6 (0.2 / RMS(O)) through a
+    plan, against the oracle's same scaling; the last matrix has a zero
+    gradient and momentum (Eq. 6: decay only)."""
+    if tile:
+        monkeypatch.setenv("MO_TILE", tile)
+    shapes = [(300, 700), (700, 300), (64, 64), (1, 300), (257, 1031), (96, 160)]
+    Ps, Gs, Ms = _mixed_state(900 + ns_steps, shapes)
+    Gs[-1].zero_()
+    Ms[-1].zero_()
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    hyp = dict(HYP, ns_steps=ns_steps)
+    H = 1024.0
+    rms = torch.full((len(Ps),), -1.0, device=DEV)
+    plan = mod.MuonPlan(Ps, Gs, Ms)
+    plan.step(update_rms=rms, scaling=scaling, hidden=H, **hyp)
+    torch.cuda.synchronize()
+    plan.close()
+    for i, shp in enumerate(shapes):
+        Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=mo.NS_COEFFS, scaling=scaling,
+                                         hidden=H, **hyp)
+        P1 = f64(Ps[i])
+        if i == len(shapes) - 1:
+            assert np.allclose(P1, P0[i] * (1 - hyp["lr"] * hyp["wd"]), rtol=1e-6, atol=0)
+            assert rms[i].item() == 0.0
+            continue
+        err = sp.rel_fro(P0[i] - P1, P0[i] - Wo)
+        print(shp, scaling, ns_steps, f"update rel_fro {err:.3e}")
+        assert err <= 2e-2, (shp, err)
+        assert abs(rms[i].item() - rms_o) <= 2e-2 * rms_o
+        if scaling == "update_norm":
+            upd = (P0[i] - P1) / hyp["lr"] - hyp["wd"] * P0[i]
+            assert abs(math.sqrt(np.mean(upd ** 2)) - 0.2) <= 2e-3
+
+
+def test_plan_scaling_validation(mod):
+    x = [randn((64, 128), 1)]
+    plan = mod.MuonPlan(x, [randn((64, 128), 2)], [torch.zeros(64, 128, device=DEV, dtype=torch.bfloat16)])
+    with pytest.raises(ValueError):
+        plan.step(lr=1e-3, scaling="hidden")          # H missing
+    with pytest.raises(mod.MuonError):
+        plan.step(lr=1e-3, scaling="hidden", hidden=0.5)
+    plan.close()
+
+
 @pytest.mark.parametrize("variant", [{"nesterov": False}, {"ns_steps": 0}, {"ns_steps": 1},
                                      {"ns_steps": 10}, {"mu": 0.0}])
 def test_step_variants(mod, variant):
