@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense800m",
                     help="dense800m (default), llama1p5b_gqa, moe_share, large_n5, "
-                         "large_n10, fp32_128x512")
+                         "large_n10, fp32_128x512, kv_heads")
     ap.add_argument("--scaling", default="shape", choices=["shape", "hidden", "update_norm"],
                     help="update scaling: 0.2 sqrt(max(A,B)) (default), 0.2 sqrt(H) with H the "
                          "largest matrix dimension, or 0.2 / RMS(X_N)")

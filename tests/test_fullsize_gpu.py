@@ -2,7 +2,8 @@
 benchmark times (one plan over every matrix of the workload, full
 workspace).
 
-* 800M dense, 1.5B GQA and the MoE share: sampled matrices (every shape
+* 800M dense, 1.5B GQA, the MoE share and the per-head split of the GQA
+  attention (960 matrices [128, 2048]): sampled matrices (every shape
   group, both orientations; for the MoE share all 32 non-expert matrices
   and 16 experts) are checked one by one against the fp64 oracle, started
   from the same pre-step state: update relative Frobenius error <= 2e-2,
@@ -76,7 +77,7 @@ def _run_step(mod, wl, T, ns_steps):
     return rms
 
 
-@pytest.mark.parametrize("key", ["dense800m", "llama1p5b_gqa", "moe_share"])
+@pytest.mark.parametrize("key", ["dense800m", "llama1p5b_gqa", "moe_share", "kv_heads"])
 def test_full_workload_sampled_parity(mod, key):
     wl = W.WORKLOADS[key]
     T = W.make_muon_tensors(wl, "cuda")

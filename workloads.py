@@ -144,6 +144,19 @@ WORKLOADS: Dict[str, Workload] = {
               MatGroup("tall", 28672, 8192, 16)),
         grad_dtype=torch.bfloat16, mom_dtype=torch.bfloat16,
         ns_dtype=torch.bfloat16, w_std=0.01),
+    "kv_heads": Workload(
+        key="kv_heads",
+        description=("the 1.5B GQA model's attention with every head a separate "
+                     "Muon matrix (head dim 128): 24 layers x (16 q, 4 k, 4 v "
+                     "heads [2048,128] and 16 o heads [128,2048]) = 960 small "
+                     "matrices"),
+        cid=7,
+        mats=(MatGroup("head_q", 2048, 128, 16 * 24),
+              MatGroup("head_k", 2048, 128, 4 * 24),
+              MatGroup("head_v", 2048, 128, 4 * 24),
+              MatGroup("head_o", 128, 2048, 16 * 24)),
+        grad_dtype=torch.bfloat16, mom_dtype=torch.bfloat16,
+        ns_dtype=torch.bfloat16),
 }
 WORKLOADS["large_n10"] = dataclasses.replace(
     WORKLOADS["large_n5"], key="large_n10", ns_steps=10, cid=6,
