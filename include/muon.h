@@ -147,7 +147,11 @@ int mo_muon_plan_create(const mo_tensor* tensors, int64_t count,
 int mo_muon_plan_workspace_size(const mo_muon_plan* plan, size_t* full_bytes,
                                 size_t* min_bytes);
 
-/* The step of mo_muon_step on a plan's tensors. */
+/* The step of mo_muon_step on a plan's tensors.  It only enqueues kernels
+ * (no allocation, memset, host copy or synchronisation), so it can be
+ * captured into a HIP graph; replays reuse the captured hyper-parameters,
+ * scaling, workspace and update_rms pointer, and read the tensors' current
+ * contents. */
 int mo_muon_plan_step(mo_muon_plan* plan, float lr, float wd, float mu,
                       int nesterov, int ns_steps, const float* abc,
                       float rms_scale, float eps, float* update_rms,
