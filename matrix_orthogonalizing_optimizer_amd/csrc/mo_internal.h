@@ -93,6 +93,25 @@ struct GemmArgs {
   int rms_only;                          // EPI_APPLY: only write the rms_part partials of x
 };
 
+// Fused Newton-Schulz + apply for matrices with m <= 128 (bf16, 128-row
+// panels): one workgroup per matrix (ns_small.hip).
+struct SmallBin {
+  const MatDesc* desc;                   // per matrix
+  void* x0; void* x1;                    // X_0 (unscaled N) and the ping-pong buffer
+  int64_t x_stride;                      // elements per matrix: 128 * n_pad
+  const float* rscale;                   // 1 / (||N||_F + eps) per matrix
+  float* rms_part;                       // [count][n_pad / 128] or null
+  int n_pad, m_true, n_true, count;
+  float step;                            // W <- W - (lrwd W + step X_N)
+};
+struct SmallArgs {
+  SmallBin bin[kMaxGroup];
+  int nbins;
+  int ns_steps;                          // >= 1
+  float a, b, c;                         // Eq. 2 coefficients
+  float lrwd;
+};
+
 // Elementwise apply for ns_steps = 0 (X_N = X_0), and for EPI_STORE with 0
 // steps in the Newton-Schulz-only entry point.
 struct ApplyX0Args {
@@ -152,6 +171,7 @@ hipError_t launch_norm(const NormArgs& a, int chunk, hipStream_t s);
 hipError_t launch_gemm(int ns_dt, TileCfg cfg, Epi epi, int waves, const GemmArgs& a,
                        hipStream_t s);
 hipError_t launch_apply_x0(const ApplyX0Args& a, int chunk, hipStream_t s);
+hipError_t launch_small(const SmallArgs& a, int total, hipStream_t s);
 hipError_t launch_rms(const RmsArgs& a, int chunk, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s);
 

@@ -478,6 +478,19 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
   return MO_OK;
 }
 
+// The fused small-matrix kernel takes a shape group when its matrices sit
+// on one 128-row panel (m <= 128, bf16) and are numerous enough to fill the
+// chip with one workgroup each; it applies with the shape or hidden scaling
+// (the update-norm scaling and the Newton-Schulz-only entry point take the
+// general kernels).
+constexpr int kSmallMinCount = 32;
+bool small_eligible(const StepCtx& c, const Item& it) {
+  const char* e = std::getenv("MO_NO_SMALL");
+  const bool off = e && std::atoi(e) != 0;
+  return !off && c.plan.ns_dt == BF16 && it.bin->cfg == TILE_128 && it.bin->m_pad == 128 &&
+         it.chunk >= kSmallMinCount && c.store_out == nullptr && c.h.scaling != MO_SCALE_UPDATE_NORM;
+}
+
 // Momentum, norm, Newton-Schulz and apply for a set of items processed
 // together (all shape groups at once when the workspace allows).
 int run_round(const StepCtx& c, std::vector<Item>& items) {
@@ -550,17 +563,46 @@ int run_round(const StepCtx& c, std::vector<Item>& items) {
       if ((rc = checked(launch_apply_x0(a, it.chunk, c.s), c.s, "apply_x0"))) return rc;
     }
   } else {
-    for (int k = 0; k < h.ns_steps; ++k) {
+    // shape groups of many small matrices (m <= 128 on 128-row panels) run
+    // the whole iteration and the apply in one fused kernel
+    std::vector<Item> small, rest;
+    for (Item& it : items) (small_eligible(c, it) ? small : rest).push_back(it);
+    for (size_t i0 = 0; i0 < small.size(); i0 += kMaxGroup) {
+      SmallArgs a{};
+      a.ns_steps = h.ns_steps;
+      a.a = h.a; a.b = h.b; a.c = h.c;
+      a.lrwd = c.lrwd;
+      int total = 0;
+      double work = 0.0;
+      for (size_t j = i0; j < std::min(small.size(), i0 + kMaxGroup); ++j) {
+        const Item& it = small[j];
+        SmallBin& sb = a.bin[a.nbins++];
+        sb.desc = it.desc;
+        sb.x0 = it.x[0]; sb.x1 = it.x[1];
+        sb.x_stride = it.L.x_elems;
+        sb.rscale = it.rscale;
+        sb.rms_part = want_rms ? it.rms_part : nullptr;
+        sb.n_pad = it.bin->n_pad; sb.m_true = it.bin->m; sb.n_true = it.bin->n;
+        sb.count = it.chunk;
+        sb.step = item_step(c, it);
+        total += it.chunk;
+        const double m = it.bin->m, n = it.bin->n;
+        work += static_cast<double>(it.chunk) * h.ns_steps * (3.0 * m * m * n + m * m * m);
+      }
+      ProfScope ps(MO_K_UPDATE, c.s, work);
+      if ((rc = checked(launch_small(a, total, c.s), c.s, "ns_small"))) return rc;
+    }
+    for (int k = 0; k < h.ns_steps && !rest.empty(); ++k) {
       const bool last = (k + 1 == h.ns_steps);
-      if ((rc = gemm_phase(c, items, EPI_GRAM, k, MO_K_GRAM, "gram"))) return rc;
-      if ((rc = gemm_phase(c, items, EPI_POLY, k, MO_K_POLY, "poly"))) return rc;
+      if ((rc = gemm_phase(c, rest, EPI_GRAM, k, MO_K_GRAM, "gram"))) return rc;
+      if ((rc = gemm_phase(c, rest, EPI_POLY, k, MO_K_POLY, "poly"))) return rc;
       const Epi ue = !last ? EPI_UPDATE : (c.store_out ? EPI_STORE : EPI_APPLY);
       if (last && unorm) {
-        if ((rc = gemm_phase(c, items, EPI_APPLY, k, MO_K_UPDATE, "update norm", true))) return rc;
-        for (Item& it : items)
+        if ((rc = gemm_phase(c, rest, EPI_APPLY, k, MO_K_UPDATE, "update norm", true))) return rc;
+        for (Item& it : rest)
           if ((rc = scale_pass(it, it.rms_part, it.L.upd_tiles, nullptr))) return rc;
       }
-      if ((rc = gemm_phase(c, items, ue, k, last ? MO_K_APPLY : MO_K_UPDATE, "update"))) return rc;
+      if ((rc = gemm_phase(c, rest, ue, k, last ? MO_K_APPLY : MO_K_UPDATE, "update"))) return rc;
     }
   }
   if (want_rms && !unorm) {

@@ -316,6 +316,62 @@ def test_step_alternative_scalings(mod, monkeypatch, scaling, ns_steps, tile):
             assert abs(math.sqrt(np.mean(upd ** 2)) - 0.2) <= 2e-3
 
 
+@pytest.mark.parametrize("ns_steps", [1, 2, 5])
+@pytest.mark.parametrize("scaling", ["shape", "hidden"])
+def test_small_matrix_fused_path(mod, ns_steps, scaling):
+    """Shape groups of >= 32 matrices with m <= 128 take the fused kernel
+    (all iterations and the apply in one workgroup per matrix): ragged and
+    oriented shapes, sampled matrices against the oracle, update RMS of
+    every matrix."""
+    groups = [((128, 512), 32), ((700, 96), 33), ((100, 300), 34), ((128, 128), 32)]
+    shapes = [s for s, n in groups for _ in range(n)]
+    Ps, Gs, Ms = _mixed_state(1300 + ns_steps, shapes)
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    hyp = dict(HYP, ns_steps=ns_steps)
+    rms = torch.zeros(len(Ps), device=DEV)
+    plan = mod.MuonPlan(Ps, Gs, Ms)
+    plan.step(update_rms=rms, scaling=scaling, hidden=512.0, **hyp)
+    torch.cuda.synchronize()
+    plan.close()
+    start = 0
+    for (shp, n) in groups:
+        for i in (start, start + n // 2, start + n - 1):
+            Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=mo.NS_COEFFS, scaling=scaling,
+                                             hidden=512.0, **hyp)
+            P1, M1 = f64(Ps[i]), f64(Ms[i])
+            err = sp.rel_fro(P0[i] - P1, P0[i] - Wo)
+            print(shp, ns_steps, scaling, f"update rel_fro {err:.3e}")
+            assert err <= 2e-2, (shp, i, err)
+            tol = np.abs(Mo) * (2.0 ** -8 + 2.0 ** -20) + (np.abs(0.95 * M0[i]) + np.abs(G0[i])) * 2.0 ** -22 + 1e-30
+            assert np.all(np.abs(M1 - Mo) <= tol)
+            assert abs(rms[i].item() - rms_o) <= 2e-2 * rms_o
+            if ns_steps == 5 and min(shp) > 1:
+                r, cc = shp
+                scale = 0.2 * (math.sqrt(512.0) if scaling == "hidden" else math.sqrt(max(r, cc)))
+                X_rec = (P0[i] - P1 - 1e-3 * 0.1 * P0[i]) / (1e-3 * scale)
+                _, N = mo.momentum_update(M0[i], G0[i], 0.95, True)
+                assert sp.per_sigma_deviation(X_rec, N, 5, eps=1e-7) <= 0.05
+        start += n
+
+
+def test_small_fused_matches_general_path(mod, monkeypatch):
+    """The fused kernel and the per-product kernels agree on the same step
+    to bf16 rounding (the iterates are rounded at the same points)."""
+    shapes = [(128, 2048)] * 40
+    outs = []
+    for off in ("0", "1"):
+        monkeypatch.setenv("MO_NO_SMALL", off)
+        Ps, Gs, Ms = _mixed_state(1400, shapes)
+        mod.muon_step(Ps, Gs, Ms, **HYP)
+        torch.cuda.synchronize()
+        outs.append([f64(p) for p in Ps])
+    P0 = f64(_mixed_state(1400, shapes)[0][0])
+    for a, b in zip(outs[0][:5], outs[1][:5]):
+        assert sp.rel_fro(P0 - a, P0 - b) <= 1e-2
+
+
 def test_plan_scaling_validation(mod):
     x = [randn((64, 128), 1)]
     plan = mod.MuonPlan(x, [randn((64, 128), 2)], [torch.zeros(64, 128, device=DEV, dtype=torch.bfloat16)])
