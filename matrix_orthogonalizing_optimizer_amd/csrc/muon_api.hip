@@ -482,13 +482,15 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
 // on one 128-row panel (m <= 128, bf16) and are numerous enough to fill the
 // chip with one workgroup each; it applies with the shape or hidden scaling
 // (the update-norm scaling and the Newton-Schulz-only entry point take the
-// general kernels).
+// general kernels).  The choice depends on the whole group, not on the
+// chunk a smaller workspace processes at a time, so results do not depend
+// on the workspace size.
 constexpr int kSmallMinCount = 32;
 bool small_eligible(const StepCtx& c, const Item& it) {
   const char* e = std::getenv("MO_NO_SMALL");
   const bool off = e && std::atoi(e) != 0;
   return !off && c.plan.ns_dt == BF16 && it.bin->cfg == TILE_128 && it.bin->m_pad == 128 &&
-         it.chunk >= kSmallMinCount && c.store_out == nullptr && c.h.scaling != MO_SCALE_UPDATE_NORM;
+         it.bin->count >= kSmallMinCount && c.store_out == nullptr && c.h.scaling != MO_SCALE_UPDATE_NORM;
 }
 
 // Momentum, norm, Newton-Schulz and apply for a set of items processed

@@ -453,7 +453,9 @@ def _run_once(mod, shapes, seed, **kw):
 
 
 def test_deterministic_and_chunking_and_plan(mod):
-    shapes = [(256, 512)] * 5 + [(512, 256)] * 3 + [(64, 1000)] * 2
+    # the 33 [128, 384] matrices take the fused small-matrix kernel, in one
+    # launch with the full workspace and one matrix at a time with the least
+    shapes = [(256, 512)] * 5 + [(512, 256)] * 3 + [(64, 1000)] * 2 + [(128, 384)] * 33
     Pa, Ma = _run_once(mod, shapes, 500)
     Pb, Mb = _run_once(mod, shapes, 500)
     for x, y in zip(Pa + Ma, Pb + Mb):
