@@ -160,3 +160,51 @@ def test_full_large_properties(mod, key):
         print(f"{key} matrix {i} [{r},{c}]: asym {asym:.2e}, |X|_2 {smax:.3f}, scaled rms {rms_scaled:.3f}")
         del A, X, P0, N
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shape", [(8192, 131072), (131072, 8192)])
+def test_max_size_matrix_properties(mod, shape):
+    """One matrix of 2^30 elements (the bf16 iterate alone is 2 GiB, so
+    byte offsets inside one matrix pass 2^31), in both orientations: the
+    momentum at sampled elements against the oracle's elementwise formula,
+    and the Newton-Schulz properties of the large-matrix test (symmetric
+    N X^T, spectral norm inside the map's band, update RMS band)."""
+    r, c = shape
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    P = torch.randn(shape, device="cuda", generator=gen) * 0.01
+    G = (torch.randn(shape, device="cuda", generator=gen) * 1e-3).to(torch.bfloat16)
+    M = torch.zeros(shape, device="cuda", dtype=torch.bfloat16)
+    idx = torch.randint(0, P.numel(), (4096,), generator=torch.Generator().manual_seed(3)).cuda()
+    g0 = f64(G.flatten()[idx])
+    P0 = P.clone()
+    rms = torch.zeros(1, device="cuda")
+    plan = mod.MuonPlan([P], [G], [M])
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    plan.step(ns_steps=5, workspace=ws, update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    plan.close()
+    del ws
+    M1 = f64(M.flatten()[idx])
+    Mo, _ = mo.momentum_update(np.zeros_like(g0), g0, 0.95, True)
+    tol = np.abs(Mo) * (2.0 ** -8 + 2.0 ** -20) + np.abs(g0) * 2.0 ** -22 + 1e-30
+    assert np.all(np.abs(M1 - Mo) <= tol)
+    step = HYP["lr"] * 0.2 * math.sqrt(max(r, c))
+    X = ((P0 - P) - HYP["lr"] * HYP["wd"] * P0) / step
+    del P0
+    N = G.float() * 1.95
+    A = (N @ X.T) if r <= c else (N.T @ X)
+    asym = (torch.linalg.norm(A - A.T) / torch.linalg.norm(A)).item()
+    assert asym <= 5e-2, asym
+    del A, N
+    v = torch.randn(X.shape[1], device="cuda")
+    for _ in range(30):
+        v = X.T @ (X @ v)
+        v = v / torch.linalg.norm(v)
+    smax = torch.linalg.norm(X @ v).item()
+    assert smax <= 1.25, smax
+    rms_scaled = 0.2 * math.sqrt(max(r, c)) * rms[0].item()
+    assert 0.05 <= rms_scaled <= 0.2 * 1.21, rms_scaled
+    print(f"{shape}: asym {asym:.2e}, |X|_2 {smax:.3f}, scaled rms {rms_scaled:.3f}")
+    del X, P, G, M
+    torch.cuda.empty_cache()
+
