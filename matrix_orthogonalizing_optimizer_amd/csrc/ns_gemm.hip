@@ -410,29 +410,43 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_sched_barrier(0);
   // one stage: substep 0, wait + barrier, substep 1 with the next stage's
   // loads; capI >= 0 adds the captured b S of row block capI (see above)
-  auto iteration = [&](int kt, auto capi) {
+  // `cb` is the stage's buffer, kt % NST: a compile-time constant in the
+  // loop unrolled by NST, so the LDS addresses of the fragment reads are too
+  auto iteration = [&](int kt, auto capi, auto cb) {
     constexpr int CI = decltype(capi)::value;
-    const int cur = kt % NST;
+    const int cur = cb;
     pipelined(S0{}, L0{}, [&](auto q) { frag1(cur, S1{}, S1{}, q); }, no_ld);
     if constexpr (CI >= 0) capture(capi, S0{}, S0{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * DPW));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
-    const int nxt = (kt + 1) % NST;
+    const int nxt = cur + 1 == NST ? 0 : cur + 1;
     const int kl = min(kt + NST, nk - 1);
     pipelined(S1{}, LD{}, [&](auto q) { frag1(nxt, S0{}, S0{}, q); },
               [&](auto q) { dma1(cur, kl, q); });
     if constexpr (CI >= 0) capture(capi, S1{}, S1{});
   };
   using NoCap = std::integral_constant<int, -1>;
-  if constexpr (!cap) {
-    for (int kt = 0; kt < nk; ++kt) iteration(kt, NoCap{});
+  // (the 4-wave 256 tile has no registers to spare for the unrolled body)
+  constexpr bool kUnroll = !(TILE == 256 && NW == 4);
+  if constexpr (!cap && !kUnroll) {
+    for (int kt = 0; kt < nk; ++kt) iteration(kt, NoCap{}, kt % NST);
+  } else if constexpr (!cap) {
+    int kt = 0;
+    for (; kt + NST <= nk; kt += NST)
+      unroll<NST>([&](auto u) {
+        iteration(kt + decltype(u)::value, NoCap{}, std::integral_constant<int, decltype(u)::value>{});
+      });
+    for (; kt < nk; ++kt) iteration(kt, NoCap{}, kt % NST);
   } else {
     // the FMM capture stages unrolled, so every accumulator index is a
     // compile-time constant
-    for (int kt = 0; kt < cap_kt; ++kt) iteration(kt, NoCap{});
-    unroll<FMM>([&](auto i) { iteration(cap_kt + decltype(i)::value, i); });
-    for (int kt = cap_kt + FMM; kt < nk; ++kt) iteration(kt, NoCap{});
+    for (int kt = 0; kt < cap_kt; ++kt) iteration(kt, NoCap{}, kt % NST);
+    unroll<FMM>([&](auto i) {
+      const int kt = cap_kt + decltype(i)::value;
+      iteration(kt, i, kt % NST);
+    });
+    for (int kt = cap_kt + FMM; kt < nk; ++kt) iteration(kt, NoCap{}, kt % NST);
   }
   // every load has landed and every wave is done with the staged tiles
   // before LDS is reused
