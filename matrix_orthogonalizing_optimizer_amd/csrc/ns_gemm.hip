@@ -213,10 +213,13 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   // contiguous block of BK rows x 64 bytes
   constexpr int kSPT = TILE / BK;                 // column stages per tile
   constexpr int kBlkBytes = BK * 64;              // bytes of one such block
-  const int nkb_b = g.N / BK;
-  auto b_koff = [&](int kt) -> int64_t {          // elements: stage kt's row block
-    const int pk = kt / kSPT, rr0 = (kt - pk * kSPT) * BK;
-    return (static_cast<int64_t>(pk) * nkb_b * TILE + rr0) * BK;
+  static_assert((kSPT & (kSPT - 1)) == 0, "stages per tile: a power of two");
+  // elements between consecutive 128/256-row panels of X (N / BK blocks of
+  // TILE x BK each)
+  const int64_t panel_elems = static_cast<int64_t>(g.N / BK) * TILE * BK;
+  auto b_koff = [&](int kt) -> int64_t {          // elements: stage kt's row block (kt >= 0)
+    const uint32_t uk = static_cast<uint32_t>(kt);
+    return static_cast<int64_t>(uk / kSPT) * panel_elems + static_cast<int64_t>((uk % kSPT) * BK * BK);
   };
 
   const int lane = tid & 63;
