@@ -415,7 +415,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   // loads; capI >= 0 adds the captured b S of row block capI (see above)
   // `cb` is the stage's buffer, kt % NST: a compile-time constant in the
   // loop unrolled by NST, so the LDS addresses of the fragment reads are too
-  auto iteration = [&](int kt, auto capi, auto cb) {
+  auto iteration = [&](int kt, auto capi, auto cb) __attribute__((always_inline)) {
     constexpr int CI = decltype(capi)::value;
     const int cur = cb;
     pipelined(S0{}, L0{}, [&](auto q) { frag1(cur, S1{}, S1{}, q); }, no_ld);
@@ -430,26 +430,32 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     if constexpr (CI >= 0) capture(capi, S1{}, S1{});
   };
   using NoCap = std::integral_constant<int, -1>;
-  // (the 4-wave 256 tile has no registers to spare for the unrolled body)
+  // stages [k0, k1): single stages up to a multiple of NST, then blocks of
+  // NST with compile-time buffers, then the rest.  (The 4-wave 256 tile has
+  // no registers to spare for the unrolled body.)
   constexpr bool kUnroll = !(TILE == 256 && NW == 4);
-  if constexpr (!cap && !kUnroll) {
-    for (int kt = 0; kt < nk; ++kt) iteration(kt, NoCap{}, kt % NST);
-  } else if constexpr (!cap) {
-    int kt = 0;
-    for (; kt + NST <= nk; kt += NST)
-      unroll<NST>([&](auto u) {
-        iteration(kt + decltype(u)::value, NoCap{}, std::integral_constant<int, decltype(u)::value>{});
-      });
-    for (; kt < nk; ++kt) iteration(kt, NoCap{}, kt % NST);
+  auto run_range = [&](int k0, int k1) __attribute__((always_inline)) {
+    int kt = k0;
+    if constexpr (kUnroll) {
+      for (; kt < k1 && kt % NST != 0; ++kt) iteration(kt, NoCap{}, kt % NST);
+      for (; kt + NST <= k1; kt += NST)
+        unroll<NST>([&](auto u) {
+          iteration(kt + decltype(u)::value, NoCap{}, std::integral_constant<int, decltype(u)::value>{});
+        });
+    }
+    for (; kt < k1; ++kt) iteration(kt, NoCap{}, kt % NST);
+  };
+  if constexpr (!cap) {
+    run_range(0, nk);
   } else {
     // the FMM capture stages unrolled, so every accumulator index is a
     // compile-time constant
-    for (int kt = 0; kt < cap_kt; ++kt) iteration(kt, NoCap{}, kt % NST);
+    run_range(0, cap_kt);
     unroll<FMM>([&](auto i) {
       const int kt = cap_kt + decltype(i)::value;
       iteration(kt, i, kt % NST);
     });
-    for (int kt = cap_kt + FMM; kt < nk; ++kt) iteration(kt, NoCap{}, kt % NST);
+    run_range(cap_kt + FMM, nk);
   }
   // every load has landed and every wave is done with the staged tiles
   // before LDS is reused
