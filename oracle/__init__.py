@@ -4,4 +4,4 @@ Imported by ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
 leg of ``bench.py``; never by the product package.
 """
 
-from . import brute, muon_oracle, spectral  # noqa: F401
+from . import brute, muon_oracle, spectral, svd_entropy  # noqa: F401
