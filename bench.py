@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--scaling", default="shape", choices=["shape", "hidden", "update_norm"],
                     help="update scaling: 0.2 sqrt(max(A,B)) (default), 0.2 sqrt(H) with H the "
                          "largest matrix dimension, or 0.2 / RMS(X_N)")
+    ap.add_argument("--svd-entropy", action="store_true",
+                    help="time the SVD-entropy diagnostic (section 3.4) over the workload's "
+                         "Muon weight matrices instead of the optimizer step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not bracket launches with HIP events")
@@ -121,6 +124,90 @@ def cpu_baseline(wl, muon_T, adam_T, budget_s: float = 30.0):
                        + f"; host has {len(os.sched_getaffinity(0))} usable cores")}
 
 
+FP64_PEAK_TFLOPS = 78.6       # fp64 vector and matrix
+
+
+def svd_main(args, torch, mo_amd, W, wl, dev):
+    """SVD entropy and singular values of every Muon weight matrix of the
+    workload (fp32 weights); a run is one mo_svd_entropy call over all of
+    them.  The roofline is that of the reduction pass (rank-2 update and
+    matrix-vector products of one Householder step), HBM-bound: its
+    algorithmic bytes are the block-lower trailing elements read (and, from
+    the second step on, written), 8 bytes each."""
+    T = W.make_muon_tensors(wl, dev)
+    mats = list(T.params)
+    full, _ = mo_amd.svd_entropy_workspace_size(tuple(x.shape) for x in mats)
+    ws = torch.empty(full, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        return mo_amd.svd_entropy(mats, sigma=True, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    classes = ["svd_gram", "svd_reduce", "svd_column", "svd_eig"]
+    mo_amd.profile_reset()
+    if not args.no_profile:
+        mo_amd.profile_enable(classes)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        h, _sig = run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mo_amd.profile_enable([])
+    prof = {c: mo_amd.profile_read(c) for c in classes}
+    ms_per_run = elapsed * 1e3 / args.steps
+    kernels = {}
+    for c in classes:
+        n, ms, work = prof[c]
+        if n:
+            unit = {"svd_gram": "TFLOP/s", "svd_eig": "Gpivot/s"}.get(c, "GB/s")
+            scale = {"TFLOP/s": 1e12, "Gpivot/s": 1e9, "GB/s": 1e9}[unit]
+            kernels[c] = {"launches": n, "ms_per_run": ms / args.steps, "mean_ms": ms / n,
+                          "rate": work / (ms * 1e-3) / scale if ms > 0 else None, "unit": unit}
+    red = prof["svd_reduce"]
+    roofline = None
+    if red[0]:
+        ach = red[2] / (red[1] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                    "kernel": "svd_trd_pass (rank-2 update + partial products, one step)",
+                    "bytes_per_launch": red[2] / red[0], "mean_launch_ms": red[1] / red[0]}
+    line = {
+        "metric": "SVD-entropy diagnostic matrices/s (section 3.4 entropy + appendix F spectrum)",
+        "value": len(mats) * 1e3 / ms_per_run, "unit": "matrices/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_run,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (seeded random-init fp32 weights of the workload)",
+        "config": {"workload": wl.key, "matrices": len(mats),
+                   "shapes": sorted({f"{g.rows}x{g.cols}" for g in wl.mats})},
+        "entropy_mean": float(h.mean()),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import svd_entropy as se
+        t_total, sample, idx = 0.0, [], 0
+        for grp in wl.mats:
+            w = mats[idx].detach().cpu().double().numpy()
+            t1 = time.perf_counter()
+            se.svd_entropy(w)
+            dt = time.perf_counter() - t1
+            t_total += dt * grp.count
+            sample.append(f"1 of {grp.count} [{grp.rows},{grp.cols}] ({dt:.2f} s)")
+            idx += grp.count
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        line["cpu_baseline"] = {
+            "value": len(mats) / t_total, "unit": "matrices/s", "cores": threads, "kind": "oracle",
+            "sample": ("fp64 numpy SVD oracle, extrapolated from " + "; ".join(sample)
+                       + f"; host has {len(os.sched_getaffinity(0))} usable cores")}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -139,6 +226,9 @@ def main():
     torch.cuda.set_device(dev)
     wl = W.WORKLOADS[args.workload]
     mo_amd._lib.lib()
+    if args.svd_entropy:
+        svd_main(args, torch, mo_amd, W, wl, dev)
+        return
 
     T = W.make_muon_tensors(wl, dev)
     A = W.make_adamw_tensors(wl, dev) if wl.vecs else None

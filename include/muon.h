@@ -15,7 +15,9 @@
  *     head parameters use AdamW with the same learning rate and decay;
  *   - section 2.3, Algorithm 1: the per-matrix update RMS is reported;
  *   - section 3.1, Eq. 5 and Eq. 6: the alternative update scalings
- *     0.2 * sqrt(H) and 0.2 / RMS(O) (mo_muon_plan_set_scaling).
+ *     0.2 * sqrt(H) and 0.2 / RMS(O) (mo_muon_plan_set_scaling);
+ *   - section 3.4 and appendix F: the SVD entropy and the sorted singular
+ *     values of weight matrices (mo_svd_entropy, a diagnostic).
  *
  * General rules for every entry point
  *   Memory   All tensor pointers are DEVICE pointers on the current HIP
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MO_ABI_VERSION 2
+#define MO_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum mo_status {
@@ -214,6 +216,42 @@ int mo_newton_schulz(const void* input, void* output, int64_t batch,
                      const float* abc, float eps, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* One matrix for the SVD-entropy diagnostic. */
+typedef struct mo_matrix {
+    const void* data;      /* device [rows, cols], row-major, 16-byte aligned */
+    int64_t     rows;
+    int64_t     cols;
+} mo_matrix;
+
+/* Workspace for mo_svd_entropy (full/min as in mo_muon_workspace_size): per
+ * matrix about 8 m (m + m / 64 + 7) bytes, m = min(rows, cols).  The
+ * matrices are checked as for mo_svd_entropy (dtype aside).  Host-only. */
+int mo_svd_entropy_workspace_size(const mo_matrix* mats, int64_t count,
+                                  size_t* full_bytes, size_t* min_bytes);
+
+/* SVD entropy (section 3.4) and singular values (appendix F) of `count`
+ * matrices, on `stream`:
+ *   entropy[i] = -(1 / log n) sum_j p_j log p_j,
+ *       p_j = sigma_j^2 / sum_l sigma_l^2, n = min(rows_i, cols_i)
+ *   (0 log 0 = 0; entropy 0 when n = 1 or the matrix is zero).
+ *   dtype: MO_F32 or MO_BF16, the element type of every matrix.
+ *   entropy: device double [count].
+ *   sigma: NULL, or device double [sum_i min(rows_i, cols_i)] that receives
+ *       each matrix's singular values, largest first, packed in the
+ *       caller's order (appendix F divides them by the first).
+ *   1 <= min(rows, cols) <= 8192 and rows * cols <= 2^31.
+ * The singular values are the square roots of the eigenvalues of the fp64
+ * Gram matrix of the short side (exact products, fp64 sums), found by a
+ * Householder reduction to tridiagonal form and bisection, all in fp64:
+ * sigma_j^2 carries an absolute error of a small multiple of
+ * (rows + cols) * 2^-52 * sigma_1^2.  Results do not depend on the
+ * workspace size or on the other matrices of the call.  Outputs may not
+ * overlap each other, an input or the workspace.
+ * Returns MO_OK, MO_EINVAL, MO_EWORKSPACE or MO_EHIP. */
+int mo_svd_entropy(const mo_matrix* mats, int64_t count, int dtype,
+                   double* entropy, double* sigma, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Kernel classes for the timing counters below. */
 typedef enum mo_kernel_class {
     MO_K_MOMENTUM = 0,     /* momentum + Nesterov + norm partials + X_0 copy */
@@ -225,7 +263,11 @@ typedef enum mo_kernel_class {
     MO_K_APPLY_X0 = 6,     /* apply for ns_steps = 0                         */
     MO_K_RMS = 7,          /* update-RMS finalisation                        */
     MO_K_ADAMW = 8,        /* AdamW elementwise                              */
-    MO_K_COUNT = 9
+    MO_K_SVD_GRAM = 9,     /* SVD entropy: fp64 Gram (block-lower tiles)     */
+    MO_K_SVD_REDUCE = 10,  /* SVD entropy: rank-2 update + products, a step  */
+    MO_K_SVD_COLUMN = 11,  /* SVD entropy: per-step reflector (one WG/matrix) */
+    MO_K_SVD_EIG = 12,     /* SVD entropy: bisection, entropy and sigma      */
+    MO_K_COUNT = 13
 } mo_kernel_class;
 
 /* Timing counters.  mo_profile_enable(mask): for every class k with bit k

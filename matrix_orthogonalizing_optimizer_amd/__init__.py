@@ -18,13 +18,13 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 
 import torch
 
-from ._lib import (KERNEL_CLASS_NAMES, MO_BF16, MO_F32, MoTensor, MuonError,  # noqa: F401
-                   check, last_error, lib)
+from ._lib import (KERNEL_CLASS_NAMES, MO_BF16, MO_F32, MoMatrix, MoTensor,  # noqa: F401
+                   MuonError, check, last_error, lib)
 
 __all__ = ["muon_step", "adamw_step", "newton_schulz", "muon_workspace_size",
-           "newton_schulz_workspace_size", "MuonPlan", "MuonAdamW",
-           "profile_enable", "profile_read", "profile_reset", "MuonError",
-           "KERNEL_CLASS_NAMES"]
+           "newton_schulz_workspace_size", "svd_entropy", "svd_entropy_workspace_size",
+           "MuonPlan", "MuonAdamW", "profile_enable", "profile_read", "profile_reset",
+           "MuonError", "KERNEL_CLASS_NAMES"]
 
 _DT = {torch.float32: MO_F32, torch.bfloat16: MO_BF16}
 
@@ -258,6 +258,51 @@ def newton_schulz(x: torch.Tensor, *, ns_steps: int = 5, abc=None, eps: float = 
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream_handle(x.device, stream)))
     return out[0] if squeeze else out
+
+
+def _mk_matrices(shapes_ptrs):
+    n = len(shapes_ptrs)
+    arr = (MoMatrix * max(n, 1))()
+    for i, (ptr, r, c) in enumerate(shapes_ptrs):
+        arr[i].data = ptr
+        arr[i].rows = r
+        arr[i].cols = c
+    return arr
+
+
+def svd_entropy_workspace_size(shapes: Iterable[Tuple[int, int]]) -> Tuple[int, int]:
+    """(full, minimum) workspace bytes of ``mo_svd_entropy`` for [rows, cols] shapes."""
+    shapes = list(shapes)
+    arr = _mk_matrices([(16, r, c) for r, c in shapes])   # placeholder aligned address
+    full, mn = ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib().mo_svd_entropy_workspace_size(arr, len(shapes), ctypes.byref(full),
+                                              ctypes.byref(mn)))
+    return full.value, mn.value
+
+
+def svd_entropy(mats: Sequence[torch.Tensor], *, sigma: bool = False,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """SVD entropy (section 3.4) of each 2-D matrix (fp32 or bf16, one dtype),
+    as an fp64 tensor [len(mats)]; with ``sigma=True`` also a list of each
+    matrix's singular values, largest first (appendix F), fp64."""
+    mats = list(mats)
+    if not mats:
+        return (torch.empty(0, dtype=torch.float64), []) if sigma else torch.empty(0, dtype=torch.float64)
+    dt = _dtype_code(_common_dtype(mats, "mats"), "mats")
+    dev = mats[0].device
+    arr = _mk_matrices([(_ptr(m),) + _shape2(m) for m in mats])
+    ent = torch.empty(len(mats), dtype=torch.float64, device=dev)
+    counts = [min(_shape2(m)) for m in mats]
+    sig = torch.empty(sum(counts), dtype=torch.float64, device=dev) if sigma else None
+    if workspace is None:
+        full, _ = svd_entropy_workspace_size(_shape2(m) for m in mats)
+        workspace = _workspace(dev, full)
+    check(lib().mo_svd_entropy(arr, len(mats), dt, _ptr(ent), _ptr(sig), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(),
+                               _stream_handle(dev, stream)))
+    if not sigma:
+        return ent
+    return ent, list(torch.split(sig, counts))
 
 
 def profile_enable(classes: Iterable[str] = ()) -> None:

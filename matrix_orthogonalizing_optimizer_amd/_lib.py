@@ -17,9 +17,11 @@ MO_OK, MO_EINVAL, MO_EUNSUPPORTED, MO_EWORKSPACE, MO_EHIP = 0, -1, -2, -3, -4
 MO_F32, MO_BF16 = 0, 1
 MO_SCALE_SHAPE, MO_SCALE_HIDDEN, MO_SCALE_UPDATE_NORM = 0, 1, 2
 (MO_K_MOMENTUM, MO_K_NORM, MO_K_GRAM, MO_K_POLY, MO_K_UPDATE, MO_K_APPLY,
- MO_K_APPLY_X0, MO_K_RMS, MO_K_ADAMW) = range(9)
+ MO_K_APPLY_X0, MO_K_RMS, MO_K_ADAMW, MO_K_SVD_GRAM, MO_K_SVD_REDUCE,
+ MO_K_SVD_COLUMN, MO_K_SVD_EIG) = range(13)
 KERNEL_CLASS_NAMES = ["momentum", "norm", "gram", "poly", "update", "apply",
-                      "apply_x0", "rms", "adamw"]
+                      "apply_x0", "rms", "adamw", "svd_gram", "svd_reduce",
+                      "svd_column", "svd_eig"]
 
 STATUS_NAMES = {MO_OK: "MO_OK", MO_EINVAL: "MO_EINVAL",
                 MO_EUNSUPPORTED: "MO_EUNSUPPORTED",
@@ -30,6 +32,10 @@ class MoTensor(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
                 ("state0", ctypes.c_void_p), ("state1", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class MoMatrix(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
 class MuonError(RuntimeError):
@@ -64,6 +70,10 @@ _SIGS = {
                                                    _c.POINTER(_c.c_size_t)]),
     "mo_newton_schulz": (_c.c_int, [_P, _P, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
                                     _c.POINTER(_c.c_float), _c.c_float, _P, _c.c_size_t, _P]),
+    "mo_svd_entropy_workspace_size": (_c.c_int, [_c.POINTER(MoMatrix), _c.c_int64,
+                                                 _c.POINTER(_c.c_size_t), _c.POINTER(_c.c_size_t)]),
+    "mo_svd_entropy": (_c.c_int, [_c.POINTER(MoMatrix), _c.c_int64, _c.c_int, _P, _P, _P,
+                                  _c.c_size_t, _P]),
     "mo_profile_enable": (_c.c_int, [_c.c_uint]),
     "mo_profile_read": (_c.c_int, [_c.c_int, _c.POINTER(_c.c_int64), _c.POINTER(_c.c_double),
                                    _c.POINTER(_c.c_double)]),

@@ -1,0 +1,454 @@
+// SVD-entropy diagnostic of weight matrices (gfx950).
+//
+// "Muon is Scalable for LLM Training", section 3.4 (singular-value spectrum
+// dynamics): the SVD entropy of a matrix with singular values sigma_1..n is
+// the entropy of p_i = sigma_i^2 / sum_j sigma_j^2 divided by log n;
+// appendix F plots the singular values, largest first, over the largest.
+//
+// sigma_i^2 are the eigenvalues of the Gram matrix S = X X^T of the matrix
+// oriented short side first (X [m, n], m = min(rows, cols)).  After reading
+// the input everything is fp64:
+//   1. svd_gram_kernel: S (block-lower 64 x 64 tiles, diagonal tiles full),
+//      exact products of the fp32/bf16 inputs, fp64 sums;
+//   2. Householder reduction of S to a symmetric tridiagonal T with the same
+//      eigenvalues.  Step k reflects with H_k = I - v_k v_k^T (|v_k|^2 = 2,
+//      support k+1 .. m-1): with p = B v_k (B the trailing block),
+//      w_k = p - (v_k^T p / 2) v_k, H B H = B - v_k w_k^T - w_k v_k^T.
+//      Two launches per step: svd_trd_col_kernel (one workgroup per matrix)
+//      finishes w_k from the partial products and builds v_{k+1} from the
+//      updated column k+1; svd_trd_pass_kernel applies step k's rank-2
+//      update to the trailing block and, in the same sweep, forms the
+//      partial products of B' v_{k+1} for the next step -- one read and one
+//      write of the block-lower trailing tiles per step;
+//   3. svd_eig_kernel: eigenvalues of T by bisection on Sturm counts (the
+//      number of negative pivots of T - x I), one lane per eigenvalue, so
+//      they come out in ascending order;
+//   4. svd_out_kernel: sigma_i^2 = max(lambda_i, 0), the entropy, and the
+//      singular values largest first.
+// Sums are taken in a fixed order: results do not depend on the batching.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+
+#include "mo_internal.h"
+
+namespace mo {
+namespace {
+
+constexpr int kT = kSvdTile;
+
+__device__ __forceinline__ double to_f64(float x) { return static_cast<double>(x); }
+__device__ __forceinline__ double to_f64(uint16_t x) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(x) << 16));
+}
+
+// Lower-triangular tile t -> (ti, tj), ti >= tj, row-major over the triangle.
+__device__ __forceinline__ void tri_tile(int t, int& ti, int& tj) {
+  int i = static_cast<int>((sqrtf(8.0f * static_cast<float>(t) + 1.0f) - 1.0f) * 0.5f);
+  while (i * (i + 1) / 2 > t) --i;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  ti = i;
+  tj = t - i * (i + 1) / 2;
+}
+
+// Sum over the workgroup in a fixed order; every thread gets the same value.
+// `sh` holds NT / 64 doubles.
+template <int NT>
+__device__ double block_sum(double x, double* sh) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < NT / 64; ++i) t += sh[i];
+  return t;
+}
+template <int NT, bool kMax>
+__device__ double block_ext(double x, double* sh) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const double y = __shfl_xor(x, o);
+    x = kMax ? fmax(x, y) : fmin(x, y);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = sh[0];
+  for (int i = 1; i < NT / 64; ++i) t = kMax ? fmax(t, sh[i]) : fmin(t, sh[i]);
+  return t;
+}
+
+// ------------------------------------------------------------------ 1. Gram
+// One 64 x 64 block-lower tile of S per workgroup (blockIdx.y: matrix of the
+// launch); K staged through LDS 32 columns at a time as fp64 [k][row].
+constexpr int kGK = 32;
+
+template <typename T>
+__device__ __forceinline__ void gram_stage(const T* __restrict__ w, const SvdGramArgs& p, int row0, int k0,
+                                           double (*xs)[kT + 1]) {
+  const int tid = threadIdx.x;
+  if (!p.trans) {
+    // X = W [m, n]: lanes along k (contiguous), 8 rows per pass
+    const int kk = tid & 31, rr = tid >> 5;
+    const int k = k0 + kk;
+#pragma unroll
+    for (int e = 0; e < kT / 8; ++e) {
+      const int r = rr + 8 * e, row = row0 + r;
+      double x = 0.0;
+      if (row < p.m && k < p.n) x = to_f64(w[static_cast<int64_t>(row) * p.ld + k]);
+      xs[kk][r] = x;
+    }
+  } else {
+    // X = W^T, W [n, m]: lanes along the row index of X (contiguous in W)
+    const int rr = tid & 63, kk = tid >> 6;
+    const int row = row0 + rr;
+#pragma unroll
+    for (int e = 0; e < kGK / 4; ++e) {
+      const int k = kk + 4 * e;
+      double x = 0.0;
+      if (row < p.m && k0 + k < p.n) x = to_f64(w[static_cast<int64_t>(k0 + k) * p.ld + row]);
+      xs[k][rr] = x;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void svd_gram_kernel(SvdGramArgs p) {
+  __shared__ double xa[kGK][kT + 1], xb[kGK][kT + 1];
+  int ti, tj;
+  tri_tile(blockIdx.x, ti, tj);
+  const T* __restrict__ w = static_cast<const T*>(p.src[blockIdx.y]);
+  double* __restrict__ s = p.dst[blockIdx.y];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int k0 = 0; k0 < p.n; k0 += kGK) {
+    gram_stage(w, p, ti * kT, k0, xa);
+    gram_stage(w, p, tj * kT, k0, xb);
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < kGK; ++k) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = xa[k][ty + 16 * i];
+        b[i] = xb[k][tx + 16 * i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = ti * kT + ty + 16 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = tj * kT + tx + 16 * j;
+      if (row < p.m && col < p.m) s[static_cast<int64_t>(row) * p.m + col] = acc[i][j];
+    }
+  }
+}
+
+// ------------------------------------------------- 2. Householder reduction
+// Step bookkeeping (k = -1 .. m - 3, j = k + 1):
+//   col(k):  [k >= 0] p_k = sum of the partial products left by pass(k - 1);
+//            w_k = p_k - (v_k . p_k / 2) v_k.  Column j of the matrix after
+//            step k: c_i = a_ij - v_k,i w_k,j - w_k,i v_k,j (i >= j); d_j = c_j.
+//            j <= m - 3: v_j from x = c_{j+1..m-1} (the reflector that maps x
+//            to (alpha, 0, ..), alpha = -sign(x_0) |x|), e_j = alpha
+//            (v_j = 0, e_j = x_0 when x is already of that form).
+//            j = m - 2: e_j = c_{m-1}; d_{m-1} = a_{m-1,m-1} - 2 v_k w_k there.
+//   pass(k): (j <= m - 3) on rows and columns >= r0 = k + 2: [k >= 0] apply
+//            a -= v_k w_k^T + w_k v_k^T; partial products of the result with
+//            v_j, one slot per 64-wide tile: the tile (I, J) (I >= J) stores
+//            its row sums in slot J of rows I and, off the diagonal, its
+//            column sums (the mirrored upper tile) in slot I of rows J.
+// Column j keeps its pre-step value in memory once read: it is never read
+// again.
+constexpr int kColThreads = 1024;
+constexpr int kColPer = kSvdMaxM / kColThreads;
+
+__global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, int k) {
+  __shared__ double red[kColThreads / 64];
+  __shared__ double bc[3];                // w_k,j and v_k,j; x_0 (separate: no reuse race)
+  const int b = blockIdx.x, tid = threadIdx.x, m = p.m, j = k + 1;
+  const double* __restrict__ a = p.a + static_cast<int64_t>(b) * m * m;
+  const double* __restrict__ vk = p.v + (static_cast<int64_t>(k & 1) * p.batch + b) * m;
+  double* __restrict__ vj = p.v + (static_cast<int64_t>((k + 1) & 1) * p.batch + b) * m;
+  double* __restrict__ w = p.w + static_cast<int64_t>(b) * m;
+  const double* __restrict__ part = p.part + static_cast<int64_t>(b) * p.nb * m;
+  double* __restrict__ d = p.d + static_cast<int64_t>(b) * m;
+  double* __restrict__ e = p.e + static_cast<int64_t>(b) * m;
+
+  double wv[kColPer], c[kColPer];
+  double wj = 0.0, vkj = 0.0;
+  if (k >= 0) {
+    const int s0 = (k + 1) / kT;          // first slot the previous pass wrote
+    double dot = 0.0;
+#pragma unroll
+    for (int q = 0; q < kColPer; ++q) {
+      const int i = tid + q * kColThreads;
+      wv[q] = 0.0;
+      if (i < m && i >= k + 1) {
+        double s = 0.0;
+        for (int sl = s0; sl < p.nb; ++sl) s += part[static_cast<int64_t>(sl) * m + i];
+        wv[q] = s;
+        dot = fma(vk[i], s, dot);
+      }
+    }
+    const double half = 0.5 * block_sum<kColThreads>(dot, red);
+#pragma unroll
+    for (int q = 0; q < kColPer; ++q) {
+      const int i = tid + q * kColThreads;
+      if (i < m) {
+        const double wi = i >= k + 1 ? wv[q] - half * vk[i] : 0.0;
+        w[i] = wi;
+        wv[q] = wi;
+        if (i == j) {
+          bc[0] = wi;
+          bc[1] = vk[i];
+        }
+      }
+    }
+    __syncthreads();
+    wj = bc[0];
+    vkj = bc[1];
+  }
+  // column j after step k
+#pragma unroll
+  for (int q = 0; q < kColPer; ++q) {
+    const int i = tid + q * kColThreads;
+    c[q] = 0.0;
+    if (i < m && i >= j) {
+      double x = a[static_cast<int64_t>(i) * m + j];
+      if (k >= 0) x -= vk[i] * wj + wv[q] * vkj;
+      c[q] = x;
+      if (i == j) d[j] = x;
+      if (j == m - 2 && i == m - 1) {
+        e[j] = x;
+        double dl = a[static_cast<int64_t>(i) * m + i];
+        if (k >= 0) dl -= 2.0 * vk[i] * wv[q];
+        d[i] = dl;
+      }
+    }
+  }
+  if (j > m - 3) return;                  // no reflector left (uniform)
+
+  double ss = 0.0;
+#pragma unroll
+  for (int q = 0; q < kColPer; ++q) {
+    const int i = tid + q * kColThreads;
+    if (i < m && i >= j + 2) ss = fma(c[q], c[q], ss);
+    if (i == j + 1) bc[2] = c[q];
+  }
+  const double sigma = block_sum<kColThreads>(ss, red);   // (its barriers publish bc[2])
+  const double x0 = bc[2];
+  double scale = 0.0, u0 = 0.0, alpha = x0;
+  if (sigma > 0.0) {
+    const double mu = sqrt(fma(x0, x0, sigma));
+    alpha = x0 >= 0.0 ? -mu : mu;
+    u0 = x0 - alpha;                      // |u0| = |x0| + mu: no cancellation
+    scale = sqrt(2.0 / fma(u0, u0, sigma));
+  }
+#pragma unroll
+  for (int q = 0; q < kColPer; ++q) {
+    const int i = tid + q * kColThreads;
+    if (i < m) vj[i] = i == j + 1 ? u0 * scale : (i >= j + 2 ? c[q] * scale : 0.0);
+  }
+  if (tid == 0) e[j] = alpha;
+}
+
+__global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int k) {
+  __shared__ double red[kT][kT + 1];
+  __shared__ double colp[4][kT];
+  const int m = p.m, r0 = k + 2, b0 = r0 / kT;
+  int ti, tj;
+  tri_tile(blockIdx.x, ti, tj);
+  const int I = b0 + ti, J = b0 + tj;
+  const int b = blockIdx.y;
+  double* __restrict__ a = p.a + static_cast<int64_t>(b) * m * m;
+  const double* __restrict__ vu = p.v + (static_cast<int64_t>(k & 1) * p.batch + b) * m;
+  const double* __restrict__ wu = p.w + static_cast<int64_t>(b) * m;
+  const double* __restrict__ vn = p.v + (static_cast<int64_t>((k + 1) & 1) * p.batch + b) * m;
+  double* __restrict__ part = p.part + static_cast<int64_t>(b) * p.nb * m;
+  const bool upd = k >= 0;
+
+  const int tid = threadIdx.x, tc = tid & 63;
+  const int tr = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = J * kT + tc;
+  const bool cok = col < m && col >= r0;
+  double vuc = 0.0, wuc = 0.0, vnc = 0.0;
+  if (cok) {
+    vnc = vn[col];
+    if (upd) {
+      vuc = vu[col];
+      wuc = wu[col];
+    }
+  }
+  double cp = 0.0;
+#pragma unroll 4
+  for (int q = 0; q < 16; ++q) {
+    const int rl = tr * 16 + q, row = I * kT + rl;
+    double prod = 0.0;
+    if (row < m && row >= r0) {
+      const double vnr = vn[row];
+      if (cok) {
+        double* ap = a + static_cast<int64_t>(row) * m + col;
+        double x = *ap;
+        if (upd) {
+          x -= vu[row] * wuc + wu[row] * vuc;
+          *ap = x;
+        }
+        prod = x * vnc;
+        cp = fma(x, vnr, cp);
+      }
+    }
+    red[rl][tc] = prod;
+  }
+  colp[tr][tc] = cp;
+  __syncthreads();
+  {
+    // row sums: four lanes per row, 16 columns each, then combined in the
+    // same order on every lane
+    const int rl = tid >> 2, qd = tid & 3;
+    double s = 0.0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) s += red[rl][qd * 16 + t];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    const int row = I * kT + rl;
+    if (qd == 0 && row < m) part[static_cast<int64_t>(J) * m + row] = s;
+  }
+  if (I != J && tid < kT) {
+    const int c2 = J * kT + tid;
+    if (c2 < m) part[static_cast<int64_t>(I) * m + c2] = (colp[0][tid] + colp[1][tid]) + (colp[2][tid] + colp[3][tid]);
+  }
+}
+
+// ------------------------------------------------------- 3. eigenvalues
+// Sturm count: the number of eigenvalues of T below x equals the number of
+// negative pivots of the LDL^T factorisation of T - x I (Sylvester's law of
+// inertia).  A pivot smaller than `pivmin` in magnitude is replaced by
+// -pivmin so that the recurrence never divides by zero.
+constexpr int kEigThreads = 256;
+
+__global__ __launch_bounds__(kEigThreads) void svd_eig_kernel(SvdEigArgs p) {
+  extern __shared__ double eig_lds[];     // d and e^2: 16 m bytes
+  __shared__ double red[kEigThreads / 64];
+  const int b = blockIdx.y, m = p.m, tid = threadIdx.x;
+  double* sd = eig_lds;
+  double* se2 = eig_lds + m;
+  const double* __restrict__ d = p.d + static_cast<int64_t>(b) * m;
+  const double* __restrict__ e = p.e + static_cast<int64_t>(b) * m;
+  double lo = DBL_MAX, hi = -DBL_MAX, emax = 0.0;
+  for (int i = tid; i < m; i += kEigThreads) {
+    const double di = d[i];
+    const double el = i > 0 ? fabs(e[i - 1]) : 0.0;
+    const double er = i < m - 1 ? fabs(e[i]) : 0.0;
+    sd[i] = di;
+    se2[i] = er * er;
+    lo = fmin(lo, di - el - er);          // Gershgorin discs
+    hi = fmax(hi, di + el + er);
+    emax = fmax(emax, er);
+  }
+  lo = block_ext<kEigThreads, false>(lo, red);
+  hi = block_ext<kEigThreads, true>(hi, red);
+  emax = block_ext<kEigThreads, true>(emax, red);
+  const double tnorm = fmax(fabs(lo), fabs(hi));
+  const double pivmin = DBL_MIN * fmax(1.0, emax * emax);
+  const double atol = DBL_EPSILON * tnorm;
+  // widen so that the counts at the ends are exactly 0 and m
+  lo -= 2.0 * DBL_EPSILON * tnorm * m + 2.0 * pivmin;
+  hi += 2.0 * DBL_EPSILON * tnorm * m + 2.0 * pivmin;
+
+  const int kk = blockIdx.x * kEigThreads + tid;
+  if (kk >= m) return;                    // no barrier follows
+  for (int it = 0; it < 128; ++it) {
+    if (hi - lo <= atol + 2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi))) break;
+    const double x = 0.5 * (lo + hi);
+    int cnt = 0;
+    double q = sd[0] - x;
+    if (fabs(q) < pivmin) q = -pivmin;
+    cnt += q < 0.0;
+    for (int i = 1; i < m; ++i) {
+      q = (sd[i] - x) - se2[i - 1] / q;
+      if (fabs(q) < pivmin) q = -pivmin;
+      cnt += q < 0.0;
+    }
+    if (cnt <= kk) lo = x;
+    else hi = x;
+  }
+  p.lam[static_cast<int64_t>(b) * m + kk] = 0.5 * (lo + hi);
+}
+
+// ------------------------------------------------- 4. entropy, sigma
+constexpr int kOutThreads = 256;
+
+__global__ __launch_bounds__(kOutThreads) void svd_out_kernel(SvdOutArgs p) {
+  __shared__ double red[kOutThreads / 64];
+  const int q = blockIdx.x, b = p.first + q, m = p.m, tid = threadIdx.x;
+  const double* __restrict__ lam = p.lam + static_cast<int64_t>(b) * m;
+  double tot = 0.0;
+  for (int i = tid; i < m; i += kOutThreads) tot += fmax(lam[i], 0.0);
+  tot = block_sum<kOutThreads>(tot, red);
+  double h = 0.0;
+  if (tot > 0.0) {
+    for (int i = tid; i < m; i += kOutThreads) {
+      const double pi = fmax(lam[i], 0.0) / tot;
+      if (pi > 0.0) h -= pi * log(pi);
+    }
+  }
+  h = block_sum<kOutThreads>(h, red);
+  if (tid == 0) p.entropy[p.out_index[q]] = (m > 1 && tot > 0.0) ? h / log(static_cast<double>(m)) : 0.0;
+  if (p.sigma) {
+    double* s = p.sigma + p.sigma_off[q];
+    for (int i = tid; i < m; i += kOutThreads) s[m - 1 - i] = sqrt(fmax(lam[i], 0.0));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_svd_gram(int dt, const SvdGramArgs& a, int count, hipStream_t s) {
+  const int nt = (a.m + kT - 1) / kT;
+  const dim3 grid(nt * (nt + 1) / 2, count);
+  if (dt == F32) hipLaunchKernelGGL(svd_gram_kernel<float>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(svd_gram_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, hipStream_t s) {
+  hipLaunchKernelGGL(svd_trd_col_kernel, dim3(a.batch), dim3(kColThreads), 0, s, a, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int k, hipStream_t s) {
+  const int t = a.nb - (k + 2) / kT;
+  hipLaunchKernelGGL(svd_trd_pass_kernel, dim3(t * (t + 1) / 2, a.batch), dim3(256), 0, s, a, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_svd_eig(const SvdEigArgs& a, int batch, hipStream_t s) {
+  // dynamic LDS above 64 KiB (m > 4096) needs the kernel's limit raised
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(svd_eig_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     2 * kSvdMaxM * static_cast<int>(sizeof(double)));
+  if (attr != hipSuccess) return attr;
+  const size_t lds = 2 * static_cast<size_t>(a.m) * sizeof(double);
+  hipLaunchKernelGGL(svd_eig_kernel, dim3((a.m + kEigThreads - 1) / kEigThreads, batch), dim3(kEigThreads), lds, s,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_svd_out(const SvdOutArgs& a, int count, hipStream_t s) {
+  hipLaunchKernelGGL(svd_out_kernel, dim3(count), dim3(kOutThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mo

@@ -221,3 +221,82 @@ def test_product_package_never_imports_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in re.sub(r"#.*|//.*", "", txt).lower().replace(
                     "oracle_", ""), f
+
+
+def _mats(shapes, base=0x10000000):
+    arr = (L.MoMatrix * max(len(shapes), 1))()
+    off = base
+    for i, (r, c) in enumerate(shapes):
+        arr[i].data, arr[i].rows, arr[i].cols = off, r, c
+        off += (r * c * 4 + 255) // 256 * 256
+    return arr
+
+
+def _svd_ws(shapes):
+    full, mn = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = L.lib().mo_svd_entropy_workspace_size(_mats(shapes), len(shapes), ctypes.byref(full),
+                                               ctypes.byref(mn))
+    return rc, full.value, mn.value
+
+
+def test_svd_entropy_workspace_size():
+    rc, full, mn = _svd_ws([(1536, 1536)] * 4 + [(6144, 1536)] * 2 + [(64, 2048)])
+    assert rc == L.MO_OK
+    # one m x m fp64 working matrix per matrix plus vectors; the m = 1536
+    # group (6 matrices, both orientations) is the largest chunk
+    assert mn >= 1536 * 1536 * 8 and full >= 6 * 1536 * 1536 * 8
+    assert full < 6 * 1536 * (1536 + 1536 // 64 + 16) * 8 + 4096
+    assert _svd_ws([(300, 40)])[1:] == _svd_ws([(40, 300)])[1:]
+    assert _svd_ws([(8193, 8193)])[0] == L.MO_EINVAL
+    assert _svd_ws([(8192, 1 << 18)])[0] == L.MO_OK
+    assert _svd_ws([(8192, (1 << 18) + 1)])[0] == L.MO_EINVAL
+
+
+@pytest.mark.parametrize("case,code", [
+    ("bad_dtype", L.MO_EINVAL), ("negative_count", L.MO_EINVAL), ("null_mats", L.MO_EINVAL),
+    ("zero_cols", L.MO_EINVAL), ("null_data", L.MO_EINVAL), ("misaligned_data", L.MO_EINVAL),
+    ("too_wide", L.MO_EINVAL), ("null_entropy", L.MO_EINVAL), ("misaligned_sigma", L.MO_EINVAL),
+    ("sigma_overlaps_input", L.MO_EINVAL), ("entropy_overlaps_sigma", L.MO_EINVAL),
+    ("ws_overlaps_input", L.MO_EINVAL), ("null_workspace", L.MO_EWORKSPACE),
+    ("small_workspace", L.MO_EWORKSPACE),
+])
+def test_svd_entropy_rejects(case, code):
+    shapes = [(64, 128), (200, 96)]
+    arr = _mats(shapes)
+    n, dt = len(shapes), L.MO_F32
+    ent, sig, ws, ws_bytes = 0x50000000, 0x51000000, 0x70000000, 1 << 40
+    if case == "bad_dtype":
+        dt = 3
+    elif case == "negative_count":
+        n = -1
+    elif case == "null_mats":
+        arr = None
+    elif case == "zero_cols":
+        arr[1].cols = 0
+    elif case == "null_data":
+        arr[0].data = None
+    elif case == "misaligned_data":
+        arr[1].data = arr[1].data + 8
+    elif case == "too_wide":
+        arr[0].rows, arr[0].cols = 9000, 9000
+    elif case == "null_entropy":
+        ent = None
+    elif case == "misaligned_sigma":
+        sig = 0x51000004
+    elif case == "sigma_overlaps_input":
+        sig = arr[1].data + 64
+    elif case == "entropy_overlaps_sigma":
+        ent = sig + 8
+    elif case == "ws_overlaps_input":
+        ws = 0x10000000 - 256
+    elif case == "null_workspace":
+        ws = None
+    elif case == "small_workspace":
+        ws_bytes = 4096
+    rc = L.lib().mo_svd_entropy(arr, n, dt, ent, sig, ws, ws_bytes, None)
+    assert rc == code, (rc, L.last_error())
+    assert L.last_error()
+
+
+def test_svd_entropy_empty_call_is_ok():
+    assert L.lib().mo_svd_entropy(None, 0, L.MO_F32, None, None, None, 0, None) == L.MO_OK
