@@ -53,6 +53,14 @@ __device__ __forceinline__ void tri_tile(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
+// Lane l's value of a double, as a wave-uniform value.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
 // Sum over the workgroup in a fixed order; every thread gets the same value.
 // `sh` holds NT / 64 doubles.
 template <int NT>
@@ -292,25 +300,33 @@ __global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int k) 
       wuc = wu[col];
     }
   }
+  // this lane's 16 elements: column col, rows rbase .. rbase + 15.  Loads
+  // go to clamped (always valid) addresses, all issued before any use, and
+  // positions outside the trailing block are masked to zero afterwards, so
+  // no load sits in a lane-divergent branch.  A row's validity is the same
+  // for every lane of the wave; the wave's 16 rows of v_k, w_k and v_j come
+  // in with one load (lanes 0-15, 16-31, 32-47) and are broadcast by lane.
+  const int rbase = I * kT + tr * 16;
+  const int colc = min(col, m - 1);
+  double x[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) x[q] = a[static_cast<int64_t>(min(rbase + q, m - 1)) * m + colc];
+  const int which = tc >> 4;
+  const double* rsrc = which == 0 ? vu : (which == 1 ? wu : vn);
+  const double rv = (which < 3 && (upd || which == 2)) ? rsrc[min(rbase + (tc & 15), m - 1)] : 0.0;
   double cp = 0.0;
-#pragma unroll 4
+#pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const int rl = tr * 16 + q, row = I * kT + rl;
-    double prod = 0.0;
-    if (row < m && row >= r0) {
-      const double vnr = vn[row];
-      if (cok) {
-        double* ap = a + static_cast<int64_t>(row) * m + col;
-        double x = *ap;
-        if (upd) {
-          x -= vu[row] * wuc + wu[row] * vuc;
-          *ap = x;
-        }
-        prod = x * vnc;
-        cp = fma(x, vnr, cp);
-      }
+    const int row = rbase + q;
+    const bool ok = cok && row < m && row >= r0;
+    double y = x[q];
+    if (upd) {
+      y -= readlane_f64(rv, q) * wuc + readlane_f64(rv, 16 + q) * vuc;
+      if (ok) a[static_cast<int64_t>(row) * m + col] = y;
     }
-    red[rl][tc] = prod;
+    y = ok ? y : 0.0;
+    cp = fma(y, readlane_f64(rv, 32 + q), cp);
+    red[tr * 16 + q][tc] = y * vnc;
   }
   colp[tr][tc] = cp;
   __syncthreads();
