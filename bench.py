@@ -132,8 +132,8 @@ def svd_main(args, torch, mo_amd, W, wl, dev):
     workload (fp32 weights); a run is one mo_svd_entropy call over all of
     them.  The roofline is that of the reduction pass (rank-2 update and
     matrix-vector products of one Householder step), HBM-bound: its
-    algorithmic bytes are the block-lower trailing elements read (and, from
-    the second step on, written), 8 bytes each."""
+    algorithmic bytes are the block-lower trailing elements it reads, 8
+    bytes each."""
     T = W.make_muon_tensors(wl, dev)
     mats = list(T.params)
     full, _ = mo_amd.svd_entropy_workspace_size(tuple(x.shape) for x in mats)
@@ -146,7 +146,7 @@ def svd_main(args, torch, mo_amd, W, wl, dev):
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    classes = ["svd_gram", "svd_reduce", "svd_column", "svd_eig"]
+    classes = ["svd_gram", "svd_reduce", "svd_panel", "svd_column", "svd_eig"]
     mo_amd.profile_reset()
     if not args.no_profile:
         mo_amd.profile_enable(classes)
@@ -173,7 +173,7 @@ def svd_main(args, torch, mo_amd, W, wl, dev):
         ach = red[2] / (red[1] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                    "kernel": "svd_trd_pass (rank-2 update + partial products, one step)",
+                    "kernel": "svd_trd_pass (matrix-vector products of one Householder step)",
                     "bytes_per_launch": red[2] / red[0], "mean_launch_ms": red[1] / red[0]}
     line = {
         "metric": "SVD-entropy diagnostic matrices/s (section 3.4 entropy + appendix F spectrum)",

@@ -224,7 +224,7 @@ typedef struct mo_matrix {
 } mo_matrix;
 
 /* Workspace for mo_svd_entropy (full/min as in mo_muon_workspace_size): per
- * matrix about 8 m (m + m / 64 + 7) bytes, m = min(rows, cols).  The
+ * matrix about 8 m (m + m / 64 + 37) bytes, m = min(rows, cols).  The
  * matrices are checked as for mo_svd_entropy (dtype aside).  Host-only. */
 int mo_svd_entropy_workspace_size(const mo_matrix* mats, int64_t count,
                                   size_t* full_bytes, size_t* min_bytes);
@@ -264,10 +264,11 @@ typedef enum mo_kernel_class {
     MO_K_RMS = 7,          /* update-RMS finalisation                        */
     MO_K_ADAMW = 8,        /* AdamW elementwise                              */
     MO_K_SVD_GRAM = 9,     /* SVD entropy: fp64 Gram (block-lower tiles)     */
-    MO_K_SVD_REDUCE = 10,  /* SVD entropy: rank-2 update + products, a step  */
+    MO_K_SVD_REDUCE = 10,  /* SVD entropy: matrix-vector products of a step  */
     MO_K_SVD_COLUMN = 11,  /* SVD entropy: per-step reflector (one WG/matrix) */
     MO_K_SVD_EIG = 12,     /* SVD entropy: bisection, entropy and sigma      */
-    MO_K_COUNT = 13
+    MO_K_SVD_PANEL = 13,   /* SVD entropy: deferred rank-2 updates of a panel */
+    MO_K_COUNT = 14
 } mo_kernel_class;
 
 /* Timing counters.  mo_profile_enable(mask): for every class k with bit k

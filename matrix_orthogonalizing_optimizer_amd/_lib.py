@@ -18,10 +18,10 @@ MO_F32, MO_BF16 = 0, 1
 MO_SCALE_SHAPE, MO_SCALE_HIDDEN, MO_SCALE_UPDATE_NORM = 0, 1, 2
 (MO_K_MOMENTUM, MO_K_NORM, MO_K_GRAM, MO_K_POLY, MO_K_UPDATE, MO_K_APPLY,
  MO_K_APPLY_X0, MO_K_RMS, MO_K_ADAMW, MO_K_SVD_GRAM, MO_K_SVD_REDUCE,
- MO_K_SVD_COLUMN, MO_K_SVD_EIG) = range(13)
+ MO_K_SVD_COLUMN, MO_K_SVD_EIG, MO_K_SVD_PANEL) = range(14)
 KERNEL_CLASS_NAMES = ["momentum", "norm", "gram", "poly", "update", "apply",
                       "apply_x0", "rms", "adamw", "svd_gram", "svd_reduce",
-                      "svd_column", "svd_eig"]
+                      "svd_column", "svd_eig", "svd_panel"]
 
 STATUS_NAMES = {MO_OK: "MO_OK", MO_EINVAL: "MO_EINVAL",
                 MO_EUNSUPPORTED: "MO_EUNSUPPORTED",

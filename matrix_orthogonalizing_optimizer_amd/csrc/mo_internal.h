@@ -168,6 +168,7 @@ constexpr int kSvdTile = 64;                 // tile edge of the Gram and reduct
 constexpr int kSvdMaxM = 8192;               // largest min(rows, cols)
 constexpr int kSvdGramBatch = 16;            // matrices per Gram launch
 constexpr int kSvdOutBatch = 64;             // matrices per entropy launch
+constexpr int kSvdPanel = 16;                // Householder steps per deferred update
 struct SvdGramArgs {
   const void* src[kSvdGramBatch];            // [rows, cols] row-major inputs (one shape per launch)
   double* dst[kSvdGramBatch];                // their m x m Gram matrices
@@ -177,10 +178,11 @@ struct SvdGramArgs {
 struct SvdTrdArgs {
   double* a;                                 // [batch][m][m] working matrices
   double* v;                                 // [2][batch][m] Householder vectors (by step parity)
-  double* w;                                 // [batch][m]
   double* part;                              // [batch][nb][m] partial products, one slot per tile column
   double* d;                                 // [batch][m] tridiagonal: diagonal
   double* e;                                 // [batch][m] tridiagonal: subdiagonal (m - 1 used)
+  double* pv;                                // [batch][kSvdPanel][m] the panel's v of each step
+  double* pw;                                // [batch][kSvdPanel][m] and its w
   int m, nb, batch;
 };
 struct SvdEigArgs {
@@ -214,9 +216,11 @@ hipError_t launch_small(const SmallArgs& a, int total, hipStream_t s);
 hipError_t launch_rms(const RmsArgs& a, int chunk, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_svd_gram(int dt, const SvdGramArgs& a, int count, hipStream_t s);
-// one step of the Householder reduction: k = -1 .. m - 3 (see the kernel)
-hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, hipStream_t s);
-hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int k, hipStream_t s);
+// one step of the Householder reduction: k = -1 .. m - 3, panel started at
+// step k0 (see the kernels)
+hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, int k0, hipStream_t s);
+hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int j, hipStream_t s);
+hipError_t launch_svd_trd_panel(const SvdTrdArgs& a, int r0, hipStream_t s);
 hipError_t launch_svd_eig(const SvdEigArgs& a, int batch, hipStream_t s);
 hipError_t launch_svd_out(const SvdOutArgs& a, int count, hipStream_t s);
 

@@ -747,7 +747,8 @@ size_t svd_chunk_bytes(int m, int64_t cnt) {
   const int64_t nb = (m + kSvdTile - 1) / kSvdTile;
   const size_t v = static_cast<size_t>(m) * sizeof(double) * static_cast<size_t>(cnt);
   return align_up(v * static_cast<size_t>(m))           // working matrices
-         + align_up(2 * v) + align_up(v)                  // Householder vectors v (2), w
+         + align_up(2 * v)                                // Householder vectors (two steps)
+         + 2 * align_up(v * kSvdPanel)                    // the panel's v and w
          + align_up(v * static_cast<size_t>(nb))          // partial products
          + 3 * align_up(v);                               // d, e, eigenvalues
 }
@@ -809,7 +810,8 @@ int svd_chunk(const std::vector<SvdItem>& items, size_t b, size_t e, int dtype, 
   SvdTrdArgs t{};
   t.a = take(v * static_cast<size_t>(m));
   t.v = take(2 * v);
-  t.w = take(v);
+  t.pv = take(v * kSvdPanel);
+  t.pw = take(v * kSvdPanel);
   t.part = take(v * static_cast<size_t>(nb));
   t.d = take(v);
   t.e = take(v);
@@ -836,19 +838,27 @@ int svd_chunk(const std::vector<SvdItem>& items, size_t b, size_t e, int dtype, 
     ProfScope ps(MO_K_SVD_GRAM, s, static_cast<double>(c) * m * m * g.n);
     if ((rc = checked(launch_svd_gram(dtype, g, c, s), s, "svd gram"))) return rc;
   }
-  // 2. Householder reduction to tridiagonal
+  // 2. Householder reduction to tridiagonal, rank-2 updates applied in
+  //    panels of kSvdPanel steps
   const int kend = std::max(m - 3, -1);
+  int k0 = 0;
   for (int k = -1; k <= kend; ++k) {
     {
-      const int64_t rows = m - (k + 1), slots = nb - (k + 1) / kSvdTile;
+      const double rows = m - (k + 1), slots = nb - (k + 1) / kSvdTile;
       ProfScope ps(MO_K_SVD_COLUMN, s, k >= 0 ? static_cast<double>(cnt) * rows * slots * 8.0 : 0.0);
-      if ((rc = checked(launch_svd_trd_col(t, k, s), s, "svd column"))) return rc;
+      if ((rc = checked(launch_svd_trd_col(t, k, k0, s), s, "svd column"))) return rc;
     }
-    if (k + 1 <= m - 3) {
-      const double tr = m - (k + 2);
-      ProfScope ps(MO_K_SVD_REDUCE, s, static_cast<double>(cnt) * tr * (tr + 1) / 2 * (k >= 0 ? 16.0 : 8.0));
-      if ((rc = checked(launch_svd_trd_pass(t, k, s), s, "svd reduce"))) return rc;
+    const int j = k + 1;
+    if (j > m - 3) continue;
+    if (k >= 0 && k - k0 + 1 == kSvdPanel) {
+      const double tr = m - (j + 1);
+      ProfScope ps(MO_K_SVD_PANEL, s, static_cast<double>(cnt) * tr * (tr + 1) / 2 * 16.0);
+      if ((rc = checked(launch_svd_trd_panel(t, j + 1, s), s, "svd panel"))) return rc;
+      k0 = j;
     }
+    const double tr = m - (j + 1);
+    ProfScope ps(MO_K_SVD_REDUCE, s, static_cast<double>(cnt) * tr * (tr + 1) / 2 * 8.0);
+    if ((rc = checked(launch_svd_trd_pass(t, j, s), s, "svd reduce"))) return rc;
   }
   // 3. eigenvalues, 4. entropy and singular values
   {

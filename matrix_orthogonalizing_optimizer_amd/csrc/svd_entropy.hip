@@ -14,12 +14,12 @@
 //      eigenvalues.  Step k reflects with H_k = I - v_k v_k^T (|v_k|^2 = 2,
 //      support k+1 .. m-1): with p = B v_k (B the trailing block),
 //      w_k = p - (v_k^T p / 2) v_k, H B H = B - v_k w_k^T - w_k v_k^T.
-//      Two launches per step: svd_trd_col_kernel (one workgroup per matrix)
-//      finishes w_k from the partial products and builds v_{k+1} from the
-//      updated column k+1; svd_trd_pass_kernel applies step k's rank-2
-//      update to the trailing block and, in the same sweep, forms the
-//      partial products of B' v_{k+1} for the next step -- one read and one
-//      write of the block-lower trailing tiles per step;
+//      The rank-2 updates are deferred over panels of 16 steps and applied
+//      together (svd_trd_panel_kernel): each step only reads the stored
+//      block-lower trailing tiles once (svd_trd_pass_kernel, products with
+//      v_k) and corrects for the panel's pending updates in
+//      svd_trd_col_kernel (one workgroup per matrix), which also builds the
+//      next reflector from the updated column;
 //   3. svd_eig_kernel: eigenvalues of T by bisection on Sturm counts (the
 //      number of negative pivots of T - x I), one lane per eigenvalue, so
 //      they come out in ascending order;
@@ -165,40 +165,102 @@ __global__ __launch_bounds__(256) void svd_gram_kernel(SvdGramArgs p) {
 }
 
 // ------------------------------------------------- 2. Householder reduction
-// Step bookkeeping (k = -1 .. m - 3, j = k + 1):
-//   col(k):  [k >= 0] p_k = sum of the partial products left by pass(k - 1);
-//            w_k = p_k - (v_k . p_k / 2) v_k.  Column j of the matrix after
-//            step k: c_i = a_ij - v_k,i w_k,j - w_k,i v_k,j (i >= j); d_j = c_j.
-//            j <= m - 3: v_j from x = c_{j+1..m-1} (the reflector that maps x
-//            to (alpha, 0, ..), alpha = -sign(x_0) |x|), e_j = alpha
-//            (v_j = 0, e_j = x_0 when x is already of that form).
-//            j = m - 2: e_j = c_{m-1}; d_{m-1} = a_{m-1,m-1} - 2 v_k w_k there.
-//   pass(k): (j <= m - 3) on rows and columns >= r0 = k + 2: [k >= 0] apply
-//            a -= v_k w_k^T + w_k v_k^T; partial products of the result with
-//            v_j, one slot per 64-wide tile: the tile (I, J) (I >= J) stores
-//            its row sums in slot J of rows I and, off the diagonal, its
-//            column sums (the mirrored upper tile) in slot I of rows J.
-// Column j keeps its pre-step value in memory once read: it is never read
-// again.
+// Step k (k = 0 .. m - 3) reflects rows and columns k+1 .. m-1 with
+// H_k = I - v_k v_k^T.  With B the current trailing block and p = B v_k,
+// w_k = p - (v_k . p / 2) v_k and H B H = B - v_k w_k^T - w_k v_k^T.
+// The rank-2 updates are deferred over a panel of up to kSvdPanel steps
+// that starts at step k0: the stored matrix A is the matrix before step k0
+// (on rows and columns >= k0 + 1), and the matrix before step k is
+//   A - sum_t (v_t w_t^T + w_t v_t^T)   over the panel's steps t < k.
+// Per step, with j = k + 1 (launch order col(-1), pass(0), col(0), [panel],
+// pass(1), col(1), ...):
+//   col(k):   [k >= 0] p_k = (sum of the slots of pass(k))
+//                            - sum_t (v_t (w_t . v_k) + w_t (v_t . v_k));
+//             w_k = p_k - (v_k . p_k / 2) v_k, recorded in the panel.
+//             Column j after step k: c_i = a_ij - sum over the panel and
+//             step k of (v_t,i w_t,j + w_t,i v_t,j), i >= j; d_j = c_j.
+//             j <= m - 3: v_j from x = c_{j+1..m-1} (the reflector mapping x
+//             to (alpha, 0, ..), alpha = -sign(x_0) |x|), e_j = alpha
+//             (v_j = 0, e_j = x_0 when x already has that form).
+//             j = m - 2: e_j = c_{m-1}; d_{m-1} from a_{m-1,m-1} the same way.
+//   panel:    once step k fills the panel (and more steps follow):
+//             A -= sum_t (v_t w_t^T + w_t v_t^T) on rows and columns >= k + 2;
+//             the next panel starts at step k + 1.
+//   pass(j):  [j <= m - 3] partial sums of A v_j over rows and columns
+//             >= j + 1 (read only), one slot per 64-wide tile: the tile (I, J),
+//             I >= J, stores its row sums in slot J of rows I and, off the
+//             diagonal, its column sums (the mirrored upper tile) in slot I of
+//             rows J.
+// Column j keeps its old value in memory once read: it is never read again.
 constexpr int kColThreads = 1024;
 constexpr int kColPer = kSvdMaxM / kColThreads;
+constexpr int kColWaves = kColThreads / 64;
+constexpr int kP = kSvdPanel;
 
-__global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, int k) {
-  __shared__ double red[kColThreads / 64];
-  __shared__ double bc[3];                // w_k,j and v_k,j; x_0 (separate: no reuse race)
+__global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, int k, int k0) {
+  __shared__ double red[kColWaves];
+  __shared__ double dots[kColWaves][2 * kP];
+  __shared__ double bc[3 + 2 * kP];       // w_k,j, v_k,j, x_0, then v_t,j and w_t,j of the panel
   const int b = blockIdx.x, tid = threadIdx.x, m = p.m, j = k + 1;
+  const int np = k >= 0 ? k - k0 : 0;     // panel steps before step k
   const double* __restrict__ a = p.a + static_cast<int64_t>(b) * m * m;
   const double* __restrict__ vk = p.v + (static_cast<int64_t>(k & 1) * p.batch + b) * m;
   double* __restrict__ vj = p.v + (static_cast<int64_t>((k + 1) & 1) * p.batch + b) * m;
-  double* __restrict__ w = p.w + static_cast<int64_t>(b) * m;
   const double* __restrict__ part = p.part + static_cast<int64_t>(b) * p.nb * m;
+  double* __restrict__ pv = p.pv + static_cast<int64_t>(b) * kP * m;
+  double* __restrict__ pw = p.pw + static_cast<int64_t>(b) * kP * m;
   double* __restrict__ d = p.d + static_cast<int64_t>(b) * m;
   double* __restrict__ e = p.e + static_cast<int64_t>(b) * m;
 
-  double wv[kColPer], c[kColPer];
+  double wv[kColPer], vkv[kColPer], c[kColPer];
   double wj = 0.0, vkj = 0.0;
   if (k >= 0) {
-    const int s0 = (k + 1) / kT;          // first slot the previous pass wrote
+    // panel dots alpha_t = w_t . v_k and beta_t = v_t . v_k (v_k is zero
+    // below k + 1): per-lane sums, wave butterflies, one combine in LDS
+    double al[kP], be[kP];
+#pragma unroll
+    for (int t = 0; t < kP; ++t) al[t] = be[t] = 0.0;
+#pragma unroll
+    for (int q = 0; q < kColPer; ++q) {
+      const int i = tid + q * kColThreads;
+      vkv[q] = 0.0;
+      if (i < m && i >= k + 1) {
+        const double x = vk[i];
+        vkv[q] = x;
+#pragma unroll
+        for (int t = 0; t < kP; ++t)
+          if (t < np) {
+            al[t] = fma(pw[static_cast<int64_t>(t) * m + i], x, al[t]);
+            be[t] = fma(pv[static_cast<int64_t>(t) * m + i], x, be[t]);
+          }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kP; ++t) {
+      if (t < np) {
+        for (int o = 32; o > 0; o >>= 1) {
+          al[t] += __shfl_xor(al[t], o);
+          be[t] += __shfl_xor(be[t], o);
+        }
+        if ((tid & 63) == 0) {
+          dots[tid >> 6][t] = al[t];
+          dots[tid >> 6][kP + t] = be[t];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kP; ++t) {
+      double sa = 0.0, sb = 0.0;
+      if (t < np)
+        for (int wv2 = 0; wv2 < kColWaves; ++wv2) {
+          sa += dots[wv2][t];
+          sb += dots[wv2][kP + t];
+        }
+      al[t] = sa;
+      be[t] = sb;
+    }
+    const int s0 = (k + 1) / kT;          // first slot pass(k) wrote
     double dot = 0.0;
 #pragma unroll
     for (int q = 0; q < kColPer; ++q) {
@@ -207,8 +269,12 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
       if (i < m && i >= k + 1) {
         double s = 0.0;
         for (int sl = s0; sl < p.nb; ++sl) s += part[static_cast<int64_t>(sl) * m + i];
+#pragma unroll
+        for (int t = 0; t < kP; ++t)
+          if (t < np)
+            s -= pv[static_cast<int64_t>(t) * m + i] * al[t] + pw[static_cast<int64_t>(t) * m + i] * be[t];
         wv[q] = s;
-        dot = fma(vk[i], s, dot);
+        dot = fma(vkv[q], s, dot);
       }
     }
     const double half = 0.5 * block_sum<kColThreads>(dot, red);
@@ -216,19 +282,29 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
     for (int q = 0; q < kColPer; ++q) {
       const int i = tid + q * kColThreads;
       if (i < m) {
-        const double wi = i >= k + 1 ? wv[q] - half * vk[i] : 0.0;
-        w[i] = wi;
+        const double wi = i >= k + 1 ? wv[q] - half * vkv[q] : 0.0;
+        pv[static_cast<int64_t>(np) * m + i] = vkv[q];
+        pw[static_cast<int64_t>(np) * m + i] = wi;
         wv[q] = wi;
         if (i == j) {
           bc[0] = wi;
-          bc[1] = vk[i];
+          bc[1] = vkv[q];
         }
       }
     }
     __syncthreads();
     wj = bc[0];
     vkj = bc[1];
+  } else {
+#pragma unroll
+    for (int q = 0; q < kColPer; ++q) wv[q] = vkv[q] = 0.0;
   }
+  // row j of the earlier panel steps (written by earlier launches)
+  if (tid < np) {
+    bc[3 + tid] = pv[static_cast<int64_t>(tid) * m + j];
+    bc[3 + kP + tid] = pw[static_cast<int64_t>(tid) * m + j];
+  }
+  __syncthreads();
   // column j after step k
 #pragma unroll
   for (int q = 0; q < kColPer; ++q) {
@@ -236,13 +312,24 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
     c[q] = 0.0;
     if (i < m && i >= j) {
       double x = a[static_cast<int64_t>(i) * m + j];
-      if (k >= 0) x -= vk[i] * wj + wv[q] * vkj;
+      double dl = 0.0;
+      const bool last = j == m - 2 && i == m - 1;
+      if (last) dl = a[static_cast<int64_t>(i) * m + i];
+#pragma unroll
+      for (int t = 0; t < kP; ++t)
+        if (t < np) {
+          const double vti = pv[static_cast<int64_t>(t) * m + i], wti = pw[static_cast<int64_t>(t) * m + i];
+          x -= vti * bc[3 + kP + t] + wti * bc[3 + t];
+          if (last) dl -= 2.0 * vti * wti;
+        }
+      if (k >= 0) {
+        x -= vkv[q] * wj + wv[q] * vkj;
+        if (last) dl -= 2.0 * vkv[q] * wv[q];
+      }
       c[q] = x;
       if (i == j) d[j] = x;
-      if (j == m - 2 && i == m - 1) {
+      if (last) {
         e[j] = x;
-        double dl = a[static_cast<int64_t>(i) * m + i];
-        if (k >= 0) dl -= 2.0 * vk[i] * wv[q];
         d[i] = dl;
       }
     }
@@ -273,78 +360,113 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
   if (tid == 0) e[j] = alpha;
 }
 
-__global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int k) {
-  __shared__ double red[kT][kT + 1];
-  __shared__ double colp[4][kT];
-  const int m = p.m, r0 = k + 2, b0 = r0 / kT;
+// Tile (I, J) of the block-lower trailing region [r0, m)^2 for blockIdx.x;
+// a lane owns column J * 64 + (lane) and rows rbase .. rbase + 15 of it.
+struct TrdTile {
+  int I, J, col, colc, rbase, tc, tr;
+  bool cok;
+};
+__device__ __forceinline__ TrdTile trd_tile(int m, int r0) {
+  TrdTile t;
   int ti, tj;
   tri_tile(blockIdx.x, ti, tj);
-  const int I = b0 + ti, J = b0 + tj;
-  const int b = blockIdx.y;
-  double* __restrict__ a = p.a + static_cast<int64_t>(b) * m * m;
-  const double* __restrict__ vu = p.v + (static_cast<int64_t>(k & 1) * p.batch + b) * m;
-  const double* __restrict__ wu = p.w + static_cast<int64_t>(b) * m;
-  const double* __restrict__ vn = p.v + (static_cast<int64_t>((k + 1) & 1) * p.batch + b) * m;
-  double* __restrict__ part = p.part + static_cast<int64_t>(b) * p.nb * m;
-  const bool upd = k >= 0;
+  t.I = r0 / kT + ti;
+  t.J = r0 / kT + tj;
+  t.tc = threadIdx.x & 63;
+  t.tr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  t.col = t.J * kT + t.tc;
+  t.colc = min(t.col, m - 1);
+  t.cok = t.col < m && t.col >= r0;
+  t.rbase = t.I * kT + t.tr * 16;
+  return t;
+}
 
-  const int tid = threadIdx.x, tc = tid & 63;
-  const int tr = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = J * kT + tc;
-  const bool cok = col < m && col >= r0;
-  double vuc = 0.0, wuc = 0.0, vnc = 0.0;
-  if (cok) {
-    vnc = vn[col];
-    if (upd) {
-      vuc = vu[col];
-      wuc = wu[col];
-    }
-  }
-  // this lane's 16 elements: column col, rows rbase .. rbase + 15.  Loads
-  // go to clamped (always valid) addresses, all issued before any use, and
-  // positions outside the trailing block are masked to zero afterwards, so
-  // no load sits in a lane-divergent branch.  A row's validity is the same
-  // for every lane of the wave; the wave's 16 rows of v_k, w_k and v_j come
-  // in with one load (lanes 0-15, 16-31, 32-47) and are broadcast by lane.
-  const int rbase = I * kT + tr * 16;
-  const int colc = min(col, m - 1);
+// pass(j): partial sums of A v_j.  Loads go to clamped (always valid)
+// addresses, all 16 issued before any use, and positions outside the
+// trailing block are masked afterwards, so no load sits in a lane-divergent
+// branch.  The wave's 16 entries of v_j (rows) come in with one load by
+// lanes 0-15 and are broadcast by lane.
+__global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int j) {
+  __shared__ double red[kT][kT + 1];
+  __shared__ double colp[4][kT];
+  const int m = p.m, r0 = j + 1;
+  const TrdTile g = trd_tile(m, r0);
+  const int b = blockIdx.y;
+  const double* __restrict__ a = p.a + static_cast<int64_t>(b) * m * m;
+  const double* __restrict__ vn = p.v + (static_cast<int64_t>(j & 1) * p.batch + b) * m;
+  double* __restrict__ part = p.part + static_cast<int64_t>(b) * p.nb * m;
+
   double x[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) x[q] = a[static_cast<int64_t>(min(rbase + q, m - 1)) * m + colc];
-  const int which = tc >> 4;
-  const double* rsrc = which == 0 ? vu : (which == 1 ? wu : vn);
-  const double rv = (which < 3 && (upd || which == 2)) ? rsrc[min(rbase + (tc & 15), m - 1)] : 0.0;
+  for (int q = 0; q < 16; ++q) x[q] = a[static_cast<int64_t>(min(g.rbase + q, m - 1)) * m + g.colc];
+  const double vnc = vn[g.colc];
+  const double rv = g.tc < 16 ? vn[min(g.rbase + g.tc, m - 1)] : 0.0;
   double cp = 0.0;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const int row = rbase + q;
-    const bool ok = cok && row < m && row >= r0;
-    double y = x[q];
-    if (upd) {
-      y -= readlane_f64(rv, q) * wuc + readlane_f64(rv, 16 + q) * vuc;
-      if (ok) a[static_cast<int64_t>(row) * m + col] = y;
-    }
-    y = ok ? y : 0.0;
-    cp = fma(y, readlane_f64(rv, 32 + q), cp);
-    red[tr * 16 + q][tc] = y * vnc;
+    const int row = g.rbase + q;
+    const double y = (g.cok && row < m && row >= r0) ? x[q] : 0.0;
+    cp = fma(y, readlane_f64(rv, q), cp);
+    red[g.tr * 16 + q][g.tc] = y * vnc;
   }
-  colp[tr][tc] = cp;
+  colp[g.tr][g.tc] = cp;
   __syncthreads();
   {
     // row sums: four lanes per row, 16 columns each, then combined in the
     // same order on every lane
-    const int rl = tid >> 2, qd = tid & 3;
+    const int rl = threadIdx.x >> 2, qd = threadIdx.x & 3;
     double s = 0.0;
 #pragma unroll
     for (int t = 0; t < 16; ++t) s += red[rl][qd * 16 + t];
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
-    const int row = I * kT + rl;
-    if (qd == 0 && row < m) part[static_cast<int64_t>(J) * m + row] = s;
+    const int row = g.I * kT + rl;
+    if (qd == 0 && row < m) part[static_cast<int64_t>(g.J) * m + row] = s;
   }
-  if (I != J && tid < kT) {
-    const int c2 = J * kT + tid;
-    if (c2 < m) part[static_cast<int64_t>(I) * m + c2] = (colp[0][tid] + colp[1][tid]) + (colp[2][tid] + colp[3][tid]);
+  if (g.I != g.J && threadIdx.x < kT) {
+    const int c2 = g.J * kT + threadIdx.x;
+    if (c2 < m)
+      part[static_cast<int64_t>(g.I) * m + c2] =
+          (colp[0][threadIdx.x] + colp[1][threadIdx.x]) + (colp[2][threadIdx.x] + colp[3][threadIdx.x]);
+  }
+}
+
+// panel: A -= sum_t (v_t w_t^T + w_t v_t^T) over the kSvdPanel steps of the
+// full panel, on the block-lower region [r0, m)^2.  The tile's rows of v_t
+// and w_t are staged in LDS (read as broadcasts); the lane's column of them
+// stays in registers.
+__global__ __launch_bounds__(256) void svd_trd_panel_kernel(SvdTrdArgs p, int r0) {
+  __shared__ double rpv[kP][kT], rpw[kP][kT];
+  const int m = p.m;
+  const TrdTile g = trd_tile(m, r0);
+  const int b = blockIdx.y;
+  double* __restrict__ a = p.a + static_cast<int64_t>(b) * m * m;
+  const double* __restrict__ pv = p.pv + static_cast<int64_t>(b) * kP * m;
+  const double* __restrict__ pw = p.pw + static_cast<int64_t>(b) * kP * m;
+
+  double x[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) x[q] = a[static_cast<int64_t>(min(g.rbase + q, m - 1)) * m + g.colc];
+  double cv[kP], cw[kP];
+#pragma unroll
+  for (int t = 0; t < kP; ++t) {
+    cv[t] = pv[static_cast<int64_t>(t) * m + g.colc];
+    cw[t] = pw[static_cast<int64_t>(t) * m + g.colc];
+  }
+  for (int f = threadIdx.x; f < kP * kT; f += 256) {
+    const int t = f / kT, rl = f % kT;
+    const int row = min(g.I * kT + rl, m - 1);
+    rpv[t][rl] = pv[static_cast<int64_t>(t) * m + row];
+    rpw[t][rl] = pw[static_cast<int64_t>(t) * m + row];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = g.rbase + q, rl = g.tr * 16 + q;
+    double u = 0.0;
+#pragma unroll
+    for (int t = 0; t < kP; ++t) u = fma(rpv[t][rl], cw[t], fma(rpw[t][rl], cv[t], u));
+    if (g.cok && row < m && row >= r0) a[static_cast<int64_t>(row) * m + g.col] = x[q] - u;
   }
 }
 
@@ -439,14 +561,20 @@ hipError_t launch_svd_gram(int dt, const SvdGramArgs& a, int count, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, hipStream_t s) {
-  hipLaunchKernelGGL(svd_trd_col_kernel, dim3(a.batch), dim3(kColThreads), 0, s, a, k);
+hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, int k0, hipStream_t s) {
+  hipLaunchKernelGGL(svd_trd_col_kernel, dim3(a.batch), dim3(kColThreads), 0, s, a, k, k0);
   return hipGetLastError();
 }
 
-hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int k, hipStream_t s) {
-  const int t = a.nb - (k + 2) / kT;
-  hipLaunchKernelGGL(svd_trd_pass_kernel, dim3(t * (t + 1) / 2, a.batch), dim3(256), 0, s, a, k);
+hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int j, hipStream_t s) {
+  const int t = a.nb - (j + 1) / kT;
+  hipLaunchKernelGGL(svd_trd_pass_kernel, dim3(t * (t + 1) / 2, a.batch), dim3(256), 0, s, a, j);
+  return hipGetLastError();
+}
+
+hipError_t launch_svd_trd_panel(const SvdTrdArgs& a, int r0, hipStream_t s) {
+  const int t = a.nb - r0 / kT;
+  hipLaunchKernelGGL(svd_trd_panel_kernel, dim3(t * (t + 1) / 2, a.batch), dim3(256), 0, s, a, r0);
   return hipGetLastError();
 }
 
