@@ -183,6 +183,7 @@ struct SvdTrdArgs {
   double* e;                                 // [batch][m] tridiagonal: subdiagonal (m - 1 used)
   double* pv;                                // [batch][kSvdPanel][m] the panel's v of each step
   double* pw;                                // [batch][kSvdPanel][m] and its w
+  double* pdot;                              // [batch][nb][2 kSvdPanel] w_t . v, v_t . v per row block
   int m, nb, batch;
 };
 struct SvdEigArgs {
@@ -219,7 +220,7 @@ hipError_t launch_svd_gram(int dt, const SvdGramArgs& a, int count, hipStream_t 
 // one step of the Householder reduction: k = -1 .. m - 3, panel started at
 // step k0 (see the kernels)
 hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, int k0, hipStream_t s);
-hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int j, hipStream_t s);
+hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int j, int np, hipStream_t s);
 hipError_t launch_svd_trd_panel(const SvdTrdArgs& a, int r0, hipStream_t s);
 hipError_t launch_svd_eig(const SvdEigArgs& a, int batch, hipStream_t s);
 hipError_t launch_svd_out(const SvdOutArgs& a, int count, hipStream_t s);

@@ -749,6 +749,7 @@ size_t svd_chunk_bytes(int m, int64_t cnt) {
   return align_up(v * static_cast<size_t>(m))           // working matrices
          + align_up(2 * v)                                // Householder vectors (two steps)
          + 2 * align_up(v * kSvdPanel)                    // the panel's v and w
+         + align_up(static_cast<size_t>(cnt) * nb * 2 * kSvdPanel * sizeof(double))   // panel dots
          + align_up(v * static_cast<size_t>(nb))          // partial products
          + 3 * align_up(v);                               // d, e, eigenvalues
 }
@@ -812,6 +813,7 @@ int svd_chunk(const std::vector<SvdItem>& items, size_t b, size_t e, int dtype, 
   t.v = take(2 * v);
   t.pv = take(v * kSvdPanel);
   t.pw = take(v * kSvdPanel);
+  t.pdot = take(static_cast<size_t>(cnt) * nb * 2 * kSvdPanel * sizeof(double));
   t.part = take(v * static_cast<size_t>(nb));
   t.d = take(v);
   t.e = take(v);
@@ -858,7 +860,7 @@ int svd_chunk(const std::vector<SvdItem>& items, size_t b, size_t e, int dtype, 
     }
     const double tr = m - (j + 1);
     ProfScope ps(MO_K_SVD_REDUCE, s, static_cast<double>(cnt) * tr * (tr + 1) / 2 * 8.0);
-    if ((rc = checked(launch_svd_trd_pass(t, j, s), s, "svd reduce"))) return rc;
+    if ((rc = checked(launch_svd_trd_pass(t, j, j - k0, s), s, "svd reduce"))) return rc;
   }
   // 3. eigenvalues, 4. entropy and singular values
   {

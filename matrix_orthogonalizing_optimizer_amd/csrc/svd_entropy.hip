@@ -175,7 +175,8 @@ __global__ __launch_bounds__(256) void svd_gram_kernel(SvdGramArgs p) {
 // Per step, with j = k + 1 (launch order col(-1), pass(0), col(0), [panel],
 // pass(1), col(1), ...):
 //   col(k):   [k >= 0] p_k = (sum of the slots of pass(k))
-//                            - sum_t (v_t (w_t . v_k) + w_t (v_t . v_k));
+//                            - sum_t (v_t (w_t . v_k) + w_t (v_t . v_k)),
+//             the dots summed from pass(k)'s per-block partials;
 //             w_k = p_k - (v_k . p_k / 2) v_k, recorded in the panel.
 //             Column j after step k: c_i = a_ij - sum over the panel and
 //             step k of (v_t,i w_t,j + w_t,i v_t,j), i >= j; d_j = c_j.
@@ -190,7 +191,8 @@ __global__ __launch_bounds__(256) void svd_gram_kernel(SvdGramArgs p) {
 //             >= j + 1 (read only), one slot per 64-wide tile: the tile (I, J),
 //             I >= J, stores its row sums in slot J of rows I and, off the
 //             diagonal, its column sums (the mirrored upper tile) in slot I of
-//             rows J.
+//             rows J.  Its diagonal tiles also form the dots of the panel's
+//             w_t and v_t with v_j over their rows (per row block).
 // Column j keeps its old value in memory once read: it is never read again.
 constexpr int kColThreads = 1024;
 constexpr int kColPer = kSvdMaxM / kColThreads;
@@ -199,7 +201,7 @@ constexpr int kP = kSvdPanel;
 
 __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, int k, int k0) {
   __shared__ double red[kColWaves];
-  __shared__ double dots[kColWaves][2 * kP];
+  __shared__ double dots[1][2 * kP];
   __shared__ double bc[3 + 2 * kP];       // w_k,j, v_k,j, x_0, then v_t,j and w_t,j of the panel
   const int b = blockIdx.x, tid = threadIdx.x, m = p.m, j = k + 1;
   const int np = k >= 0 ? k - k0 : 0;     // panel steps before step k
@@ -215,52 +217,22 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
   double wv[kColPer], vkv[kColPer], c[kColPer];
   double wj = 0.0, vkj = 0.0;
   if (k >= 0) {
-    // panel dots alpha_t = w_t . v_k and beta_t = v_t . v_k (v_k is zero
-    // below k + 1): per-lane sums, wave butterflies, one combine in LDS
-    double al[kP], be[kP];
-#pragma unroll
-    for (int t = 0; t < kP; ++t) al[t] = be[t] = 0.0;
+    // panel dots alpha_t = w_t . v_k, beta_t = v_t . v_k: sums of the
+    // per-row-block partials of pass(k), in block order
+    const int s0 = (k + 1) / kT;          // first slot / row block pass(k) wrote
+    const double* __restrict__ pdot = p.pdot + static_cast<int64_t>(b) * p.nb * 2 * kP;
+    if (tid < 2 * kP) {
+      double acc = 0.0;
+      if ((tid < kP ? tid : tid - kP) < np)
+        for (int sl = s0; sl < p.nb; ++sl) acc += pdot[sl * 2 * kP + tid];
+      dots[0][tid] = acc;
+    }
 #pragma unroll
     for (int q = 0; q < kColPer; ++q) {
       const int i = tid + q * kColThreads;
-      vkv[q] = 0.0;
-      if (i < m && i >= k + 1) {
-        const double x = vk[i];
-        vkv[q] = x;
-#pragma unroll
-        for (int t = 0; t < kP; ++t)
-          if (t < np) {
-            al[t] = fma(pw[static_cast<int64_t>(t) * m + i], x, al[t]);
-            be[t] = fma(pv[static_cast<int64_t>(t) * m + i], x, be[t]);
-          }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kP; ++t) {
-      if (t < np) {
-        for (int o = 32; o > 0; o >>= 1) {
-          al[t] += __shfl_xor(al[t], o);
-          be[t] += __shfl_xor(be[t], o);
-        }
-        if ((tid & 63) == 0) {
-          dots[tid >> 6][t] = al[t];
-          dots[tid >> 6][kP + t] = be[t];
-        }
-      }
+      vkv[q] = (i < m && i >= k + 1) ? vk[i] : 0.0;
     }
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < kP; ++t) {
-      double sa = 0.0, sb = 0.0;
-      if (t < np)
-        for (int wv2 = 0; wv2 < kColWaves; ++wv2) {
-          sa += dots[wv2][t];
-          sb += dots[wv2][kP + t];
-        }
-      al[t] = sa;
-      be[t] = sb;
-    }
-    const int s0 = (k + 1) / kT;          // first slot pass(k) wrote
     double dot = 0.0;
 #pragma unroll
     for (int q = 0; q < kColPer; ++q) {
@@ -272,7 +244,7 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
 #pragma unroll
         for (int t = 0; t < kP; ++t)
           if (t < np)
-            s -= pv[static_cast<int64_t>(t) * m + i] * al[t] + pw[static_cast<int64_t>(t) * m + i] * be[t];
+            s -= pv[static_cast<int64_t>(t) * m + i] * dots[0][t] + pw[static_cast<int64_t>(t) * m + i] * dots[0][kP + t];
         wv[q] = s;
         dot = fma(vkv[q], s, dot);
       }
@@ -386,7 +358,7 @@ __device__ __forceinline__ TrdTile trd_tile(int m, int r0) {
 // trailing block are masked afterwards, so no load sits in a lane-divergent
 // branch.  The wave's 16 entries of v_j (rows) come in with one load by
 // lanes 0-15 and are broadcast by lane.
-__global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int j) {
+__global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int j, int np) {
   __shared__ double red[kT][kT + 1];
   __shared__ double colp[4][kT];
   const int m = p.m, r0 = j + 1;
@@ -428,6 +400,30 @@ __global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int j) 
     if (c2 < m)
       part[static_cast<int64_t>(g.I) * m + c2] =
           (colp[0][threadIdx.x] + colp[1][threadIdx.x]) + (colp[2][threadIdx.x] + colp[3][threadIdx.x]);
+  }
+  if (g.I == g.J) {
+    // panel dots over this row block: lane = row, wave tr takes t = tr, tr + 4, ..
+    const int row = g.I * kT + g.tc;
+    const bool rok = row < m && row >= r0;
+    const double vr = rok ? vn[row] : 0.0;
+    const double* __restrict__ pv = p.pv + static_cast<int64_t>(b) * kP * m;
+    const double* __restrict__ pw = p.pw + static_cast<int64_t>(b) * kP * m;
+    double* __restrict__ pdot = p.pdot + (static_cast<int64_t>(b) * p.nb + g.I) * 2 * kP;
+    for (int t = g.tr; t < np; t += 4) {
+      double sa = 0.0, sb = 0.0;
+      if (rok) {
+        sa = pw[static_cast<int64_t>(t) * m + row] * vr;
+        sb = pv[static_cast<int64_t>(t) * m + row] * vr;
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        sa += __shfl_xor(sa, o);
+        sb += __shfl_xor(sb, o);
+      }
+      if (g.tc == 0) {
+        pdot[t] = sa;
+        pdot[kP + t] = sb;
+      }
+    }
   }
 }
 
@@ -566,9 +562,9 @@ hipError_t launch_svd_trd_col(const SvdTrdArgs& a, int k, int k0, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int j, hipStream_t s) {
+hipError_t launch_svd_trd_pass(const SvdTrdArgs& a, int j, int np, hipStream_t s) {
   const int t = a.nb - (j + 1) / kT;
-  hipLaunchKernelGGL(svd_trd_pass_kernel, dim3(t * (t + 1) / 2, a.batch), dim3(256), 0, s, a, j);
+  hipLaunchKernelGGL(svd_trd_pass_kernel, dim3(t * (t + 1) / 2, a.batch), dim3(256), 0, s, a, j, np);
   return hipGetLastError();
 }
 
