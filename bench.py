@@ -37,12 +37,13 @@ HBM_PEAK_GBS = 8000.0
 HYPER = dict(lr=1e-3, wd=0.1, mu=0.95, nesterov=True, rms_scale=0.2, eps=1e-7)
 
 
-def measured_traffic(workload: str, epi: int = 2):
-    """Calibrated HBM bytes per dispatch of the update GEMM from the committed
-    rocprofv3 counter summary (profiles/hbm_traffic_<workload>.json), or None
-    when there is none or the kernel sources changed since it was taken."""
+def measured_traffic(name: str, match):
+    """Calibrated HBM bytes per dispatch of the kernels whose names `match`
+    accepts, from the committed rocprofv3 counter summary
+    (profiles/hbm_traffic_<name>.json), or None when there is none or the
+    kernel sources listed there changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -52,13 +53,17 @@ def measured_traffic(workload: str, epi: int = 2):
     if h.hexdigest() != rec["source_sha256"]:
         return None
     n = b = 0.0
-    for name, k in rec["kernels"].items():
-        # mo::ns_gemm_kernel<T, TILE, EPI, WAVES>
-        targs = name[name.find("<") + 1:name.rfind(">")].split(",")
-        if name.startswith("mo::ns_gemm_kernel") and len(targs) > 2 and int(targs[2]) == epi:
+    for kname, k in rec["kernels"].items():
+        if match(kname):
             n += k["dispatches"]
             b += k["dispatches"] * k["hbm_bytes_per_dispatch"]
     return b / n if n else None
+
+
+def _is_update_gemm(name: str) -> bool:
+    # mo::ns_gemm_kernel<T, TILE, EPI, WAVES>, EPI 2 = the update product
+    targs = name[name.find("<") + 1:name.rfind(">")].split(",")
+    return name.startswith("mo::ns_gemm_kernel") and len(targs) > 2 and int(targs[2]) == 2
 
 
 def parse():
@@ -172,7 +177,9 @@ def svd_main(args, torch, mo_amd, W, wl, dev):
     if red[0]:
         ach = red[2] / (red[1] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                    "frac": ach / HBM_PEAK_GBS,
+                    "traffic": measured_traffic(f"svd_entropy_{wl.key}",
+                                                lambda n: n.endswith("svd_trd_pass_kernel")),
                     "kernel": "svd_trd_pass (matrix-vector products of one Householder step)",
                     "bytes_per_launch": red[2] / red[0], "mean_launch_ms": red[1] / red[0]}
     line = {
@@ -281,7 +288,7 @@ def main():
     if upd[0]:
         ach = upd[2] / (upd[1] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                    "frac": ach / peak, "traffic": measured_traffic(wl.key),
+                    "frac": ach / peak, "traffic": measured_traffic(wl.key, _is_update_gemm),
                     "kernel": "ns_gemm update X <- aX + PX",
                     "flops_per_launch": upd[2] / upd[0], "mean_launch_ms": upd[1] / upd[0]}
     ew_bytes = wl.n_elems * W.muon_elementwise_bytes_per_elem(wl) + \

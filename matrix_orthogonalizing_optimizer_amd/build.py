@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
-SOURCES = ["ns_gemm.hip", "ns_small.hip", "elementwise.hip", "svd_entropy.hip", "muon_api.hip"]
+SOURCES = ["ns_gemm.hip", "ns_small.hip", "elementwise.hip", "svd_entropy.hip", "muon_api.hip",
+           "svd_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

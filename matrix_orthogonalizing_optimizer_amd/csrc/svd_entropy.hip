@@ -32,7 +32,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "mo_internal.h"
+#include "svd_internal.h"
 
 namespace mo {
 namespace {
