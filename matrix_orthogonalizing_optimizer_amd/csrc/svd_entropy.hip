@@ -8,8 +8,8 @@
 // sigma_i^2 are the eigenvalues of the Gram matrix S = X X^T of the matrix
 // oriented short side first (X [m, n], m = min(rows, cols)).  After reading
 // the input everything is fp64:
-//   1. svd_gram_kernel: S (block-lower 64 x 64 tiles, diagonal tiles full),
-//      exact products of the fp32/bf16 inputs, fp64 sums;
+//   1. svd_gram_kernel: S (block-lower 128 x 128 tiles, diagonal tiles
+//      full): exact products of the fp32/bf16 inputs, fp64 sums;
 //   2. Householder reduction of S to a symmetric tridiagonal T with the same
 //      eigenvalues.  Step k reflects with H_k = I - v_k v_k^T (|v_k|^2 = 2,
 //      support k+1 .. m-1): with p = B v_k (B the trailing block),
@@ -88,77 +88,114 @@ __device__ double block_ext(double x, double* sh) {
 }
 
 // ------------------------------------------------------------------ 1. Gram
-// One 64 x 64 block-lower tile of S per workgroup (blockIdx.y: matrix of the
-// launch); K staged through LDS 32 columns at a time as fp64 [k][row].
-constexpr int kGK = 32;
+// One 128 x 128 block-lower tile of S per workgroup (blockIdx.y: matrix of
+// the launch), fp64 FMA on the vector ALU: thread (ty, tx) of a 16 x 16 grid
+// owns rows ty + 16 a and columns tx + 16 b (a, b < 8), so its LDS reads are
+// either shared by 16 lanes or 16 consecutive doubles.  (On this chip fp64
+// FMA on the vector ALU outruns fp64 MFMA: about 68 against 49 TFLOP/s
+// measured.)  K is staged through LDS 32 columns at a time as fp64
+// [k][row], rows padded to 129 so the transposed stores spread over the
+// banks; the next chunk's global loads are issued into registers before the
+// current chunk's products.  A diagonal tile computes its whole 128 x 128
+// block, which covers the diagonal 64 x 64 tiles in full.
+constexpr int kGT = 128;                  // output tile edge
+constexpr int kGK = 32;                   // K per LDS stage
+constexpr int kGLd = kGT + 1;             // LDS row stride (doubles)
+
+// The thread's share of one operand chunk: rows row0 .. row0 + 127 of X,
+// K columns k0 .. k0 + 31, 16 elements per thread.
+template <typename T>
+struct GramChunk {
+  T v[16];
+};
 
 template <typename T>
-__device__ __forceinline__ void gram_stage(const T* __restrict__ w, const SvdGramArgs& p, int row0, int k0,
-                                           double (*xs)[kT + 1]) {
+__device__ __forceinline__ void gram_fetch(const T* __restrict__ w, const SvdGramArgs& p, int row0, int k0,
+                                           GramChunk<T>& f) {
   const int tid = threadIdx.x;
   if (!p.trans) {
-    // X = W [m, n]: lanes along k (contiguous), 8 rows per pass
+    // X = W [m, n]: 32 lanes along k (contiguous), 8 rows per pass
     const int kk = tid & 31, rr = tid >> 5;
     const int k = k0 + kk;
+    const int kc = min(k, p.n - 1);
 #pragma unroll
-    for (int e = 0; e < kT / 8; ++e) {
-      const int r = rr + 8 * e, row = row0 + r;
-      double x = 0.0;
-      if (row < p.m && k < p.n) x = to_f64(w[static_cast<int64_t>(row) * p.ld + k]);
-      xs[kk][r] = x;
+    for (int e = 0; e < 16; ++e) {
+      const int row = row0 + rr + 8 * e;
+      const T x = w[static_cast<int64_t>(min(row, p.m - 1)) * p.ld + kc];   // clamped: always valid
+      f.v[e] = (row < p.m && k < p.n) ? x : T(0);
     }
   } else {
     // X = W^T, W [n, m]: lanes along the row index of X (contiguous in W)
-    const int rr = tid & 63, kk = tid >> 6;
+    const int rr = tid & 127, kk = tid >> 7;
     const int row = row0 + rr;
+    const int rc = min(row, p.m - 1);
 #pragma unroll
-    for (int e = 0; e < kGK / 4; ++e) {
-      const int k = kk + 4 * e;
-      double x = 0.0;
-      if (row < p.m && k0 + k < p.n) x = to_f64(w[static_cast<int64_t>(k0 + k) * p.ld + row]);
-      xs[k][rr] = x;
+    for (int e = 0; e < 16; ++e) {
+      const int k = k0 + kk + 2 * e;
+      const T x = w[static_cast<int64_t>(min(k, p.n - 1)) * p.ld + rc];       // clamped: always valid
+      f.v[e] = (row < p.m && k < p.n) ? x : T(0);
     }
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void svd_gram_kernel(SvdGramArgs p) {
-  __shared__ double xa[kGK][kT + 1], xb[kGK][kT + 1];
+__device__ __forceinline__ void gram_store(const SvdGramArgs& p, const GramChunk<T>& f, double* xs) {
+  const int tid = threadIdx.x;
+  if (!p.trans) {
+    const int kk = tid & 31, rr = tid >> 5;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xs[kk * kGLd + rr + 8 * e] = to_f64(f.v[e]);
+  } else {
+    const int rr = tid & 127, kk = tid >> 7;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xs[(kk + 2 * e) * kGLd + rr] = to_f64(f.v[e]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void svd_gram_kernel(SvdGramArgs p) {
+  __shared__ double xa[kGK * kGLd], xb[kGK * kGLd];
   int ti, tj;
   tri_tile(blockIdx.x, ti, tj);
   const T* __restrict__ w = static_cast<const T*>(p.src[blockIdx.y]);
   double* __restrict__ s = p.dst[blockIdx.y];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  double acc[4][4];
+  double acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  GramChunk<T> fa, fb;
+  gram_fetch(w, p, ti * kGT, 0, fa);
+  gram_fetch(w, p, tj * kGT, 0, fb);
   for (int k0 = 0; k0 < p.n; k0 += kGK) {
-    gram_stage(w, p, ti * kT, k0, xa);
-    gram_stage(w, p, tj * kT, k0, xb);
+    gram_store(p, fa, xa);
+    gram_store(p, fb, xb);
     __syncthreads();
-#pragma unroll 4
+    if (k0 + kGK < p.n) {
+      gram_fetch(w, p, ti * kGT, k0 + kGK, fa);
+      gram_fetch(w, p, tj * kGT, k0 + kGK, fb);
+    }
     for (int k = 0; k < kGK; ++k) {
-      double a[4], b[4];
+      double a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = xa[k][ty + 16 * i];
-        b[i] = xb[k][tx + 16 * i];
+      for (int i = 0; i < 8; ++i) {
+        a[i] = xa[k * kGLd + ty + 16 * i];
+        b[i] = xb[k * kGLd + tx + 16 * i];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = ti * kT + ty + 16 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int row = ti * kGT + ty + 16 * i;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = tj * kT + tx + 16 * j;
+    for (int j = 0; j < 8; ++j) {
+      const int col = tj * kGT + tx + 16 * j;
       if (row < p.m && col < p.m) s[static_cast<int64_t>(row) * p.m + col] = acc[i][j];
     }
   }
@@ -550,7 +587,7 @@ __global__ __launch_bounds__(kOutThreads) void svd_out_kernel(SvdOutArgs p) {
 }  // namespace
 
 hipError_t launch_svd_gram(int dt, const SvdGramArgs& a, int count, hipStream_t s) {
-  const int nt = (a.m + kT - 1) / kT;
+  const int nt = (a.m + kGT - 1) / kGT;
   const dim3 grid(nt * (nt + 1) / 2, count);
   if (dt == F32) hipLaunchKernelGGL(svd_gram_kernel<float>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(svd_gram_kernel<uint16_t>, grid, dim3(256), 0, s, a);

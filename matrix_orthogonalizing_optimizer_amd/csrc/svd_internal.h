@@ -15,7 +15,7 @@ namespace mo {
 // diagonal tiles in full) are kept.
 constexpr int kSvdTile = 64;                 // tile edge of the Gram and reduction passes
 constexpr int kSvdMaxM = 8192;               // largest min(rows, cols)
-constexpr int kSvdGramBatch = 16;            // matrices per Gram launch
+constexpr int kSvdGramBatch = 192;           // matrices per Gram launch (kernel arguments < 4 KiB)
 constexpr int kSvdOutBatch = 64;             // matrices per entropy launch
 constexpr int kSvdPanel = 16;                // Householder steps per deferred update
 struct SvdGramArgs {
