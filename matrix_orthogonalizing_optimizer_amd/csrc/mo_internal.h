@@ -76,6 +76,8 @@ struct GemmBin {
   void* out;  int64_t s_out;             // EPI_STORE output base, stride
   float* rms_part;                       // [batch][tiles_per_mat] or null
   int M, N, K;                           // padded sizes (tile multiples)
+  int k_loop;                            // K stages visited: the padded K / stage depth, or fewer
+                                         // when the tail stages multiply zero padding only
   int tiles_m, tiles_n, tiles_per_mat, batch;
   int m_true, n_true;
   float step;                            // EPI_APPLY: W <- W - (lrwd W + step x)

@@ -420,6 +420,7 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
     int per_xcd = 0;
     bool all_super = true;
     const bool want_rms = c.update_rms != nullptr && c.store_out == nullptr;
+    const int bk = 64 / c.esz;              // K elements per stage (64 bytes)
     for (size_t j = i0; j < i1; ++j) {
       const Item& it = items[order[j]];
       const Bin& bin = *it.bin;
@@ -436,6 +437,7 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
         gb.B = xc; gb.sB = it.L.x_elems;
         gb.C = it.S; gb.sC = it.L.s_elems;
         gb.M = bin.m_pad; gb.N = bin.m_pad; gb.K = bin.n_pad;
+        gb.k_loop = gb.K / bk;
         gb.tiles_m = tm; gb.tiles_n = tm; gb.tiles_per_mat = tm * (tm + 1) / 2;
         work += it.chunk * m * m * n;
       } else if (epi == EPI_POLY) {     // P' = a I + b S + c S S
@@ -444,12 +446,16 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
         gb.D = it.S; gb.sD = it.L.s_elems;
         gb.C = it.P; gb.sC = it.L.s_elems;
         gb.M = bin.m_pad; gb.N = bin.m_pad; gb.K = bin.m_pad;
+        gb.k_loop = gb.K / bk;
         gb.tiles_m = tm; gb.tiles_n = tm; gb.tiles_per_mat = tm * (tm + 1) / 2;
         work += it.chunk * m * m * m;
       } else {                          // X' = P' X, X read K-major from its own layout
         gb.A = it.P; gb.sA = it.L.s_elems;
         gb.B = xc; gb.sB = it.L.x_elems;
         gb.M = bin.m_pad; gb.N = bin.n_pad; gb.K = bin.m_pad;
+        // K runs over the rows of X: stages past the true m multiply the
+        // zero padding of P' and X only
+        gb.k_loop = (bin.m + bk - 1) / bk;
         gb.tiles_m = tm; gb.tiles_n = tn; gb.tiles_per_mat = tm * tn;
         if (epi == EPI_UPDATE) {
           gb.C = xn; gb.sC = it.L.x_elems;

@@ -202,8 +202,10 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     else grouped_tile(t, g.tiles_m, g.tiles_n, ti, tj);
   }
 
-  // row panels ti of A and tj of B: nk stages of TILE x BK each
+  // row panels ti of A and tj of B: nk stages of TILE x BK each, of which
+  // the first nkl are visited (the rest multiply zero padding)
   const int nk = g.K / BK;
+  const int nkl = g.k_loop;
   const int64_t stage_elems = static_cast<int64_t>(TILE) * BK;
   const T* __restrict__ Ag = static_cast<const T*>(g.A) + b * g.sA + static_cast<int64_t>(ti) * nk * stage_elems;
   const T* __restrict__ Bg = kNN ? static_cast<const T*>(g.B) + b * g.sB
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   // part of stage kt + 1 is visible and buffer kt % NST (fully read) may be
   // refilled.  The barrier carries no memory fence: a fence would wait for
   // every outstanding load.
-  for (int s = 0; s < NST; ++s) dma(s, min(s, nk - 1));
+  for (int s = 0; s < NST; ++s) dma(s, min(s, nkl - 1));
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 1) * DPW));
   barrier();
   unroll<kReads>([&](auto q) { frag1(0, S0{}, S0{}, q); });
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
     const int nxt = cur + 1 == NST ? 0 : cur + 1;
-    const int kl = min(kt + NST, nk - 1);
+    const int kl = min(kt + NST, nkl - 1);
     pipelined(S1{}, LD{}, [&](auto q) { frag1(nxt, S0{}, S0{}, q); },
               [&](auto q) { dma1(cur, kl, q); });
     if constexpr (CI >= 0) capture(capi, S1{}, S1{});
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     for (; kt < k1; ++kt) iteration(kt, NoCap{}, kt % NST);
   };
   if constexpr (!cap) {
-    run_range(0, nk);
+    run_range(0, nkl);
   } else {
     // the FMM capture stages unrolled, so every accumulator index is a
     // compile-time constant
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
       const int kt = cap_kt + decltype(i)::value;
       iteration(kt, i, kt % NST);
     });
-    run_range(cap_kt + FMM, nk);
+    run_range(cap_kt + FMM, nkl);
   }
   // every load has landed and every wave is done with the staged tiles
   // before LDS is reused
