@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kOutThreads) void svd_out_kernel(SvdOutArgs p) {
 hipError_t launch_svd_gram(int dt, const SvdGramArgs& a, int count, hipStream_t s) {
   const int nt = (a.m + kGT - 1) / kGT;
   const dim3 grid(nt * (nt + 1) / 2, count);
-  if (dt == F32) hipLaunchKernelGGL(svd_gram_kernel<float>, grid, dim3(256), 0, s, a);
+  if (dt == MO_F32) hipLaunchKernelGGL(svd_gram_kernel<float>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(svd_gram_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

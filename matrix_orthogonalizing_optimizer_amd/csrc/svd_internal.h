@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "mo_internal.h"
+#include "muon.h"
 
 namespace mo {
 
