@@ -32,13 +32,21 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 
 // Load 4 consecutive elements [off, off + nvalid) of a fp32 or bf16 array;
 // missing ones read as 0.  `vec` = the 4 are in range and 4-aligned.
+// kNT: the data is touched once per step, so the vector accesses carry the
+// non-temporal hint (streamed past the caches instead of filling them).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+template <bool kNT = false>
 __device__ __forceinline__ void load4(const void* base, int dt, int64_t off, int nvalid,
                                       bool vec, float v[4]) {
   if (dt == F32) {
     const float* p = static_cast<const float*>(base) + off;
     if (vec) {
-      const float4 q = *reinterpret_cast<const float4*>(p);
-      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      f32x4v q;
+      if constexpr (kNT) q = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+      else q = *reinterpret_cast<const f32x4v*>(p);
+      v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = j < nvalid ? p[j] : 0.0f;
@@ -46,9 +54,11 @@ __device__ __forceinline__ void load4(const void* base, int dt, int64_t off, int
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(base) + off;
     if (vec) {
-      const uint2 q = *reinterpret_cast<const uint2*>(p);
-      v[0] = bf2f(q.x & 0xffffu); v[1] = bf2f(q.x >> 16);
-      v[2] = bf2f(q.y & 0xffffu); v[3] = bf2f(q.y >> 16);
+      u32x2v q;
+      if constexpr (kNT) q = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p));
+      else q = *reinterpret_cast<const u32x2v*>(p);
+      v[0] = bf2f(q[0] & 0xffffu); v[1] = bf2f(q[0] >> 16);
+      v[2] = bf2f(q[1] & 0xffffu); v[3] = bf2f(q[1] >> 16);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = j < nvalid ? bf2f(p[j]) : 0.0f;
@@ -56,12 +66,15 @@ __device__ __forceinline__ void load4(const void* base, int dt, int64_t off, int
   }
 }
 
+template <bool kNT = false>
 __device__ __forceinline__ void store4(void* base, int dt, int64_t off, int nvalid,
                                        bool vec, const float v[4]) {
   if (dt == F32) {
     float* p = static_cast<float*>(base) + off;
     if (vec) {
-      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+      const f32x4v q = {v[0], v[1], v[2], v[3]};
+      if constexpr (kNT) __builtin_nontemporal_store(q, reinterpret_cast<f32x4v*>(p));
+      else *reinterpret_cast<f32x4v*>(p) = q;
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -70,10 +83,10 @@ __device__ __forceinline__ void store4(void* base, int dt, int64_t off, int nval
   } else {
     uint16_t* p = static_cast<uint16_t*>(base) + off;
     if (vec) {
-      uint2 q;
-      q.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
-      q.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
-      *reinterpret_cast<uint2*>(p) = q;
+      const u32x2v q = {static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16),
+                        static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16)};
+      if constexpr (kNT) __builtin_nontemporal_store(q, reinterpret_cast<u32x2v*>(p));
+      else *reinterpret_cast<u32x2v*>(p) = q;
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -130,16 +143,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
       const int64_t off = static_cast<int64_t>(r) * B + c;
       const bool vec = vec_ok && nvalid == 4;
       float g[4], m[4];
-      load4(md.grad, p.grad_dt, off, nvalid, vec, g);
+      load4<true>(md.grad, p.grad_dt, off, nvalid, vec, g);
       if (p.has_mom) {
-        load4(md.mom, p.mom_dt, off, nvalid, vec, m);
+        load4<true>(md.mom, p.mom_dt, off, nvalid, vec, m);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float mn = p.mu * m[j] + g[j];
           m[j] = mn;
           n4[j] = p.nesterov ? p.mu * mn + g[j] : mn;
         }
-        store4(md.mom, p.mom_dt, off, nvalid, vec, m);
+        store4<true>(md.mom, p.mom_dt, off, nvalid, vec, m);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) n4[j] = g[j];
@@ -277,10 +290,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
     const int nvalid = static_cast<int>(min<int64_t>(4, T.n - off));
     const bool vec = nvalid == 4;
     float g[4], w[4], m[4], v[4];
-    load4(T.g, p.grad_dt, off, nvalid, vec, g);
-    load4(T.p, F32, off, nvalid, vec, w);
-    load4(T.m, F32, off, nvalid, vec, m);
-    load4(T.v, F32, off, nvalid, vec, v);
+    load4<true>(T.g, p.grad_dt, off, nvalid, vec, g);
+    load4<true>(T.p, F32, off, nvalid, vec, w);
+    load4<true>(T.m, F32, off, nvalid, vec, m);
+    load4<true>(T.v, F32, off, nvalid, vec, v);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       m[j] = p.beta1 * m[j] + ob1 * g[j];
@@ -288,9 +301,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
       const float upd = (m[j] * p.bc1) / (sqrtf(v[j]) * p.bc2_rsqrt + p.eps);
       w[j] = w[j] - (p.lr * upd + lrwd * w[j]);
     }
-    store4(T.p, F32, off, nvalid, vec, w);
-    store4(T.m, F32, off, nvalid, vec, m);
-    store4(T.v, F32, off, nvalid, vec, v);
+    store4<true>(T.p, F32, off, nvalid, vec, w);
+    store4<true>(T.m, F32, off, nvalid, vec, m);
+    store4<true>(T.v, F32, off, nvalid, vec, v);
   }
 }
 
