@@ -259,10 +259,16 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
     const int s0 = (k + 1) / kT;          // first slot / row block pass(k) wrote
     const double* __restrict__ pdot = p.pdot + static_cast<int64_t>(b) * p.nb * 2 * kP;
     if (tid < 2 * kP) {
-      double acc = 0.0;
-      if ((tid < kP ? tid : tid - kP) < np)
-        for (int sl = s0; sl < p.nb; ++sl) acc += pdot[sl * 2 * kP + tid];
-      dots[0][tid] = acc;
+      double a4[4] = {0.0, 0.0, 0.0, 0.0};
+      if ((tid < kP ? tid : tid - kP) < np) {
+        int sl = s0;
+        for (; sl + 4 <= p.nb; sl += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a4[u] += pdot[(sl + u) * 2 * kP + tid];
+        }
+        for (int u = 0; sl < p.nb; ++sl, ++u) a4[u] += pdot[sl * 2 * kP + tid];
+      }
+      dots[0][tid] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
     }
 #pragma unroll
     for (int q = 0; q < kColPer; ++q) {
@@ -276,8 +282,16 @@ __global__ __launch_bounds__(kColThreads) void svd_trd_col_kernel(SvdTrdArgs p, 
       const int i = tid + q * kColThreads;
       wv[q] = 0.0;
       if (i < m && i >= k + 1) {
-        double s = 0.0;
-        for (int sl = s0; sl < p.nb; ++sl) s += part[static_cast<int64_t>(sl) * m + i];
+        // four independent partial sums (loads in flight together), combined
+        // in a fixed order
+        double s4[4] = {0.0, 0.0, 0.0, 0.0};
+        int sl = s0;
+        for (; sl + 4 <= p.nb; sl += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) s4[u] += part[static_cast<int64_t>(sl + u) * m + i];
+        }
+        for (int u = 0; sl < p.nb; ++sl, ++u) s4[u] += part[static_cast<int64_t>(sl) * m + i];
+        double s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
 #pragma unroll
         for (int t = 0; t < kP; ++t)
           if (t < np)
