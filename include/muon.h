@@ -239,7 +239,8 @@ int mo_svd_entropy_workspace_size(const mo_matrix* mats, int64_t count,
  *   sigma: NULL, or device double [sum_i min(rows_i, cols_i)] that receives
  *       each matrix's singular values, largest first, packed in the
  *       caller's order (appendix F divides them by the first).
- *   1 <= min(rows, cols) <= 8192 and rows * cols <= 2^31.
+ *   1 <= min(rows, cols) <= 8192, max(rows, cols) < 2^31 and
+ *   rows * cols <= 2^31.
  * The singular values are the square roots of the eigenvalues of the fp64
  * Gram matrix of the short side (exact products, fp64 sums), found by a
  * Householder reduction to tridiagonal form and bisection, all in fp64:

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <vector>
 
@@ -57,7 +58,8 @@ int svd_validate(const mo_matrix* mats, int64_t count, int dtype, std::vector<Sv
     const int64_t m = std::min(x.rows, x.cols), n = std::max(x.rows, x.cols);
     if (m > kSvdMaxM) return fail(MO_EINVAL, "matrix %lld: min(rows, cols) = %lld exceeds %d", static_cast<long long>(i),
                                   static_cast<long long>(m), kSvdMaxM);
-    if (n > (int64_t{1} << 31) / m) return fail(MO_EINVAL, "matrix %lld: more than 2^31 elements", static_cast<long long>(i));
+    if (n > (int64_t{1} << 31) / m || n > INT32_MAX)
+      return fail(MO_EINVAL, "matrix %lld: more than 2^31 elements, or a side of 2^31", static_cast<long long>(i));
     if (!x.data) return fail(MO_EINVAL, "matrix %lld: data is NULL", static_cast<long long>(i));
     if (!aligned16(x.data)) return fail(MO_EINVAL, "matrix %lld: data must be 16-byte aligned", static_cast<long long>(i));
     items.push_back({i, x.rows, x.cols, x.data, off, static_cast<int>(m), static_cast<int>(n)});

@@ -251,6 +251,8 @@ def test_svd_entropy_workspace_size():
     assert _svd_ws([(8193, 8193)])[0] == L.MO_EINVAL
     assert _svd_ws([(8192, 1 << 18)])[0] == L.MO_OK
     assert _svd_ws([(8192, (1 << 18) + 1)])[0] == L.MO_EINVAL
+    assert _svd_ws([(1, (1 << 31) - 1)])[0] == L.MO_OK
+    assert _svd_ws([((1 << 31), 1)])[0] == L.MO_EINVAL        # a side must fit in 32 bits
 
 
 @pytest.mark.parametrize("case,code", [
