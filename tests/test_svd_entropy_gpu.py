@@ -176,3 +176,33 @@ def test_svd_entropy_layer_shapes_against_oracle():
     torch.cuda.synchronize()
     for x, hh, ss in zip(xs, h, sig):
         _check(x, hh, ss)
+
+
+@pytest.mark.parametrize("key", ["dense800m", "moe_share"])
+def test_svd_entropy_full_workload(key):
+    """The benchmark's launch configuration: one call over every Muon weight
+    matrix of the workload (fp32 weights, full workspace).  Every matrix:
+    singular values in decreasing order, entropy in [0, 1], and the trace
+    identity sum sigma_i^2 = ||W||_F^2 (holds at any size).  One matrix per
+    shape group against the oracle."""
+    import workloads as W
+
+    wl = W.WORKLOADS[key]
+    T = W.make_muon_tensors(wl, torch.device("cuda"))
+    mats = list(T.params)
+    h, sig = mo.svd_entropy(mats, sigma=True)
+    torch.cuda.synchronize()
+    hh = h.cpu().numpy()
+    assert np.all(hh >= 0.0) and np.all(hh <= 1.0 + 1e-12)
+    for x, s in zip(mats, sig):
+        r, c = x.shape
+        s2 = s.cpu().numpy() ** 2
+        assert np.all(np.diff(s2) <= 0.0)
+        fro2 = float(torch.sum(x.double() ** 2))
+        # each sigma_i^2 within eps sigma_1^2, so the sum within m eps sigma_1^2
+        assert abs(float(np.sum(s2)) - fro2) <= min(r, c) * _eps(r, c) * float(s2[0]), (r, c)
+    start = 0
+    for g in wl.mats:
+        i = start + g.count // 2
+        _check(mats[i], h[i], sig[i])
+        start += g.count
