@@ -13,7 +13,7 @@ namespace mo {
 // m = min(rows, cols); their m x m fp64 Gram matrices sit back to back in
 // the workspace, row-major, of which the block-lower 64 x 64 tiles (the
 // diagonal tiles in full) are kept.
-constexpr int kSvdTile = 64;                 // tile edge of the Gram and reduction passes
+constexpr int kSvdTile = 64;                 // tile edge of the reduction passes (partial-product slots)
 constexpr int kSvdMaxM = 8192;               // largest min(rows, cols)
 constexpr int kSvdGramBatch = 192;           // matrices per Gram launch (kernel arguments < 4 KiB)
 constexpr int kSvdOutBatch = 64;             // matrices per entropy launch
