@@ -74,13 +74,21 @@ def _shape2(t: torch.Tensor) -> Tuple[int, int]:
 _WS: dict = {}
 
 
-def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A cached per-device byte buffer of at least ``nbytes``."""
-    key = (device.type, device.index)
+def _workspace(device: torch.device, nbytes: int, stream_handle: int) -> torch.Tensor:
+    """A cached byte buffer of at least ``nbytes`` for one (device, stream).
+    Calls queued on different streams never share it, and it is allocated on
+    that stream, so torch's allocator orders any reuse of its memory after
+    the work queued there."""
+    key = (device.type, device.index, int(stream_handle or 0))
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
         _WS.pop(key, None)
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        n = max(nbytes, 256)
+        if stream_handle and stream_handle != torch.cuda.current_stream(device).cuda_stream:
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
+                ws = torch.empty(n, dtype=torch.uint8, device=device)
+        else:
+            ws = torch.empty(n, dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
 
@@ -137,14 +145,15 @@ def muon_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
     ndt = _dtype_code(ns_dtype, "ns_dtype")
     arr = _mk_tensors(params, grads, moms)
     full, mn = muon_workspace_size([_shape2(p) for p in params], ns_dtype)
+    sh = _stream_handle(dev, stream)
     if workspace is None:
-        workspace = _workspace(dev, full)
+        workspace = _workspace(dev, full, sh)
     if update_rms is not None and (update_rms.dtype != torch.float32 or update_rms.numel() < n):
         raise ValueError("update_rms must be float32 with one slot per matrix")
     check(lib().mo_muon_step(arr, n, gdt, mdt, ndt, lr, wd, mu, int(nesterov), ns_steps,
                              _abc(abc), rms_scale, eps, _ptr(update_rms), _ptr(workspace),
                              workspace.numel() * workspace.element_size(),
-                             _stream_handle(dev, stream)))
+                             sh))
 
 
 _SCALINGS = {"shape": 0, "hidden": 1, "update_norm": 2}
@@ -188,12 +197,12 @@ class MuonPlan:
             raise ValueError('scaling="hidden" needs hidden=H')
         check(lib().mo_muon_plan_set_scaling(self._h, _SCALINGS[scaling],
                                              float(hidden) if hidden is not None else 0.0))
+        sh = _stream_handle(self.device, stream)
         if workspace is None:
-            workspace = _workspace(self.device, self.workspace_bytes)
+            workspace = _workspace(self.device, self.workspace_bytes, sh)
         check(lib().mo_muon_plan_step(self._h, lr, wd, mu, int(nesterov), ns_steps, _abc(abc),
                                       rms_scale, eps, _ptr(update_rms), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(),
-                                      _stream_handle(self.device, stream)))
+                                      workspace.numel() * workspace.element_size(), sh))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
@@ -252,11 +261,11 @@ def newton_schulz(x: torch.Tensor, *, ns_steps: int = 5, abc=None, eps: float = 
     if out is None:
         out = torch.empty_like(x3)
     ws_need = newton_schulz_workspace_size(b, r, c, x.dtype)
+    sh = _stream_handle(x.device, stream)
     if workspace is None:
-        workspace = _workspace(x.device, ws_need)
+        workspace = _workspace(x.device, ws_need, sh)
     check(lib().mo_newton_schulz(_ptr(x3), _ptr(out), b, r, c, dt, ns_steps, _abc(abc), eps,
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream_handle(x.device, stream)))
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), sh))
     return out[0] if squeeze else out
 
 
@@ -294,12 +303,12 @@ def svd_entropy(mats: Sequence[torch.Tensor], *, sigma: bool = False,
     ent = torch.empty(len(mats), dtype=torch.float64, device=dev)
     counts = [min(_shape2(m)) for m in mats]
     sig = torch.empty(sum(counts), dtype=torch.float64, device=dev) if sigma else None
+    sh = _stream_handle(dev, stream)
     if workspace is None:
         full, _ = svd_entropy_workspace_size(_shape2(m) for m in mats)
-        workspace = _workspace(dev, full)
+        workspace = _workspace(dev, full, sh)
     check(lib().mo_svd_entropy(arr, len(mats), dt, _ptr(ent), _ptr(sig), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(),
-                               _stream_handle(dev, stream)))
+                               workspace.numel() * workspace.element_size(), sh))
     if not sigma:
         return ent
     return ent, list(torch.split(sig, counts))

@@ -542,3 +542,30 @@ def test_optimizer_front(mod):
     z = np.zeros_like(before[3])
     Wo, _, _ = mo.adamw_step(before[3], grads[3], z, z, lr=1e-3, wd=0.1, t=1)
     _adamw_close(before[3], f64(vecs[0]), Wo)
+
+
+def test_steps_on_two_streams_use_separate_workspaces(mod):
+    """Two independent steps queued on two streams through the binding's
+    implicit workspaces (cached per device and stream) give the same bits as
+    the same steps run one after the other on one stream."""
+    shapes_a = [(300, 700), (1031, 257)]
+    shapes_b = [(512, 1536), (128, 128)]
+    ref = []
+    for seed, shapes in ((700, shapes_a), (800, shapes_b)):
+        Ps, Gs, Ms = _mixed_state(seed, shapes)
+        mod.muon_step(Ps, Gs, Ms, **HYP)
+        ref.append((Ps, Ms))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()     # default priority
+    A = _mixed_state(700, shapes_a)
+    B = _mixed_state(800, shapes_b)
+    torch.cuda.synchronize()
+    for _ in range(3):                                     # fresh state each round
+        Pa, Ga, Ma = [x.clone() for x in A[0]], A[1], [x.clone() for x in A[2]]
+        Pb, Gb, Mb = [x.clone() for x in B[0]], B[1], [x.clone() for x in B[2]]
+        torch.cuda.synchronize()
+        mod.muon_step(Pa, Ga, Ma, stream=s1, **HYP)
+        mod.muon_step(Pb, Gb, Mb, stream=s2, **HYP)
+        torch.cuda.synchronize()
+        for got, want in zip(Pa + Ma + Pb + Mb, ref[0][0] + ref[0][1] + ref[1][0] + ref[1][1]):
+            assert torch.equal(got, want)
