@@ -283,27 +283,38 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
   const AdamTensor T = p.t[k];
   const int64_t base = (static_cast<int64_t>(blockIdx.x) - T.block0) * kAdamElemsPerBlock;
   const float ob1 = p.one_m_beta1, ob2 = p.one_m_beta2, lrwd = p.lr * p.wd;
+  // kParts groups of 4 elements per thread: every load is issued before any
+  // arithmetic or store (the stores may alias the next group's loads, so the
+  // compiler would not hoist them by itself)
+  constexpr int kParts = kAdamElemsPerBlock / 1024;
+  float g[kParts][4], w[kParts][4], m[kParts][4], v[kParts][4];
+  int nv[kParts];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int64_t off = base + half * 1024 + threadIdx.x * 4;
-    if (off >= T.n) continue;
-    const int nvalid = static_cast<int>(min<int64_t>(4, T.n - off));
-    const bool vec = nvalid == 4;
-    float g[4], w[4], m[4], v[4];
-    load4<true>(T.g, p.grad_dt, off, nvalid, vec, g);
-    load4<true>(T.p, F32, off, nvalid, vec, w);
-    load4<true>(T.m, F32, off, nvalid, vec, m);
-    load4<true>(T.v, F32, off, nvalid, vec, v);
+  for (int h = 0; h < kParts; ++h) {
+    const int64_t off = base + h * 1024 + threadIdx.x * 4;
+    nv[h] = static_cast<int>(max<int64_t>(0, min<int64_t>(4, T.n - off)));
+    if (nv[h] == 0) continue;
+    const bool vec = nv[h] == 4;
+    load4<true>(T.g, p.grad_dt, off, nv[h], vec, g[h]);
+    load4<true>(T.p, F32, off, nv[h], vec, w[h]);
+    load4<true>(T.m, F32, off, nv[h], vec, m[h]);
+    load4<true>(T.v, F32, off, nv[h], vec, v[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < kParts; ++h) {
+    if (nv[h] == 0) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      m[j] = p.beta1 * m[j] + ob1 * g[j];
-      v[j] = p.beta2 * v[j] + ob2 * g[j] * g[j];
-      const float upd = (m[j] * p.bc1) / (sqrtf(v[j]) * p.bc2_rsqrt + p.eps);
-      w[j] = w[j] - (p.lr * upd + lrwd * w[j]);
+      m[h][j] = p.beta1 * m[h][j] + ob1 * g[h][j];
+      v[h][j] = p.beta2 * v[h][j] + ob2 * g[h][j] * g[h][j];
+      const float upd = (m[h][j] * p.bc1) / (sqrtf(v[h][j]) * p.bc2_rsqrt + p.eps);
+      w[h][j] = w[h][j] - (p.lr * upd + lrwd * w[h][j]);
     }
-    store4<true>(T.p, F32, off, nvalid, vec, w);
-    store4<true>(T.m, F32, off, nvalid, vec, m);
-    store4<true>(T.v, F32, off, nvalid, vec, v);
+    const int64_t off = base + h * 1024 + threadIdx.x * 4;
+    const bool vec = nv[h] == 4;
+    store4<true>(T.p, F32, off, nv[h], vec, w[h]);
+    store4<true>(T.m, F32, off, nv[h], vec, m[h]);
+    store4<true>(T.v, F32, off, nv[h], vec, v[h]);
   }
 }
 
