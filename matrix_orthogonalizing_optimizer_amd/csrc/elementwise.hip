@@ -114,6 +114,11 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 // The Newton-Schulz input is written once, in the oriented layout
 // [m_pad, n_pad]: straight through for a wide parameter, transposed through
 // an LDS tile for a tall one (its columns are the rows of X).
+// kAhead: every load of the thread's four rows is issued before any
+// arithmetic or store (the momentum stores may alias later rows' loads, so
+// the compiler would not hoist them by itself).  It pays for 8-byte (bf16)
+// gradient loads; with 16-byte fp32 loads the row-by-row order is as fast.
+template <bool kAhead>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   __shared__ float tile[64][65];
   __shared__ float red[4];
@@ -134,6 +139,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
 
   const int c = tb * 64 + tx * 4;
   const int nvalid = max(0, min(4, B - c));
+  float g[4][4], m[4][4];
+  if constexpr (kAhead) {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int r = ta * 64 + ty + pass * 16;
+      if (r < A && nvalid > 0) {
+        const int64_t off = static_cast<int64_t>(r) * B + c;
+        const bool vec = vec_ok && nvalid == 4;
+        load4<true>(md.grad, p.grad_dt, off, nvalid, vec, g[pass]);
+        if (p.has_mom) load4<true>(md.mom, p.mom_dt, off, nvalid, vec, m[pass]);
+      }
+    }
+  }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int rl = ty + pass * 16;
@@ -142,20 +160,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     if (r < A && nvalid > 0) {
       const int64_t off = static_cast<int64_t>(r) * B + c;
       const bool vec = vec_ok && nvalid == 4;
-      float g[4], m[4];
-      load4<true>(md.grad, p.grad_dt, off, nvalid, vec, g);
+      if constexpr (!kAhead) {
+        load4<true>(md.grad, p.grad_dt, off, nvalid, vec, g[pass]);
+        if (p.has_mom) load4<true>(md.mom, p.mom_dt, off, nvalid, vec, m[pass]);
+      }
       if (p.has_mom) {
-        load4<true>(md.mom, p.mom_dt, off, nvalid, vec, m);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float mn = p.mu * m[j] + g[j];
-          m[j] = mn;
-          n4[j] = p.nesterov ? p.mu * mn + g[j] : mn;
+          const float mn = p.mu * m[pass][j] + g[pass][j];
+          m[pass][j] = mn;
+          n4[j] = p.nesterov ? p.mu * mn + g[pass][j] : mn;
         }
-        store4<true>(md.mom, p.mom_dt, off, nvalid, vec, m);
+        store4<true>(md.mom, p.mom_dt, off, nvalid, vec, m[pass]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) n4[j] = g[j];
+        for (int j = 0; j < 4; ++j) n4[j] = g[pass][j];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -319,7 +338,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
 }
 
 hipError_t launch_prep(const PrepArgs& a, int chunk, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
+  if (a.grad_dt == BF16) hipLaunchKernelGGL(prep_kernel<true>, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(prep_kernel<false>, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_norm(const NormArgs& a, int chunk, hipStream_t s) {
