@@ -1,0 +1,57 @@
+"""The benchmark's output contract on the GPU: one JSON line with the
+required keys, a roofline object for the dominant kernel, and the oracle's
+CPU baseline (default run); the SVD-entropy mode likewise."""
+
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+        "scaling", "vs_baseline", "dtype", "data", "config", "roofline"}
+ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+
+
+def _run(args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, r.stdout
+    return json.loads(lines[0])
+
+
+def _check_common(d, steps, warmup):
+    assert KEYS <= set(d), KEYS - set(d)
+    assert d["n_gpus"] == 1 and d["steps"] == steps and d["warmup"] == warmup
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert "workload" in d["config"]
+    roof = d["roofline"]
+    assert ROOF <= set(roof), ROOF - set(roof)
+    assert 0 < roof["frac"] < 1 and abs(roof["achieved"] / roof["peak"] - roof["frac"]) < 1e-9
+    assert roof["traffic"] is None or roof["traffic"] > 0
+
+
+def test_bench_default_line():
+    d = _run(["--steps", "2", "--warmup", "1"])
+    _check_common(d, 2, 1)
+    assert d["config"]["workload"] == "dense800m" and d["unit"] == "steps/s"
+    assert d["roofline"]["bound"] == "mfma" and d["roofline"]["unit"] == "TFLOP/s"
+    cpu = d["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+
+
+def test_bench_svd_entropy_line():
+    d = _run(["--svd-entropy", "--workload", "llama1p5b_gqa", "--steps", "1", "--warmup", "0",
+              "--no-cpu-baseline"])
+    _check_common(d, 1, 0)
+    assert d["unit"] == "matrices/s" and d["dtype"] == "f64"
+    assert d["roofline"]["bound"] == "hbm" and d["roofline"]["unit"] == "GB/s"
+    assert 0.0 < d["entropy_mean"] <= 1.0
