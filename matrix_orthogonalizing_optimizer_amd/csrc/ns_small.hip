@@ -30,19 +30,25 @@ constexpr int kT = 128;                 // panel height / output tile edge
 constexpr int kBK = 32;                 // bf16 elements per 64-byte row piece
 constexpr int kCPR = 4;                 // 16-byte chunks per row piece
 constexpr int kNT = 512;                // threads
-constexpr int kNST = 3;                 // ring stages
 constexpr int kStage = kT * kCPR;       // chunks of one [128 rows][64 B] stage (8 KiB)
+constexpr int kSub = 2;                 // K-stages per ring slot (one barrier pair per slot)
+constexpr int kSlot = kSub * kStage;
+constexpr int kNST = 2;                 // ring slots
 // LDS map in 16-byte chunks.  P', S and the X' tile are [4 K-stages][128
-// rows][64 B] (chunks permuted per row as in global memory); the ring holds
-// Gram stages [128 rows][64 B] or update blocks [4 column blocks][32 rows]
-// [64 B].  The apply stages fp32 x over the S and X' regions and the tail.
-constexpr int kOffP = 0;
-constexpr int kOffRing = kOffP + 4 * kStage;
-constexpr int kOffS = kOffRing + kNST * kStage;
+// rows][64 B] (chunks permuted per row as in global memory); a ring slot
+// holds kSub Gram stages [128 rows][64 B] or kSub update blocks [4 column
+// blocks][32 rows][64 B].  The apply stages fp32 x over the S and X'
+// regions and the tail.  S and X' come first: the LDS instructions' 16-bit
+// immediate offsets then reach every access to them from one lane base,
+// which keeps the kernel within its registers.
+constexpr int kOffS = 0;
 constexpr int kOffX = kOffS + 4 * kStage;
-constexpr int kOffEnd = kOffX + 4 * kStage + 256;
+constexpr int kOffRing = kOffX + 4 * kStage + 256;
+constexpr int kOffP = kOffRing + kNST * kSlot;
+constexpr int kOffEnd = kOffP + 4 * kStage;
 constexpr int kApLd = kT + 4;           // padded fp32 row of the apply staging
-static_assert((kOffEnd - kOffS) * 4 >= kT * kApLd, "apply staging fits");
+static_assert((kOffRing - kOffS) * 4 >= kT * kApLd, "apply staging fits");
+static_assert(kOffEnd * 16 <= 160 * 1024, "LDS");
 
 }  // namespace
 
@@ -145,36 +151,49 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
     });
   };
 
-  // -------- the streamed loads: one 1 KiB piece per wave per stage
-  auto dma_gram = [&](int buf, int kt) {
-    const char* src = reinterpret_cast<const char*>(x0 + kt * (kT * kBK)) + wave * 1024;
-    lds_dma16(src, lane16, __builtin_amdgcn_readfirstlane(lds_addr(smem + kOffRing + buf * kStage + wave * 64)));
+  // -------- the streamed loads: one 1 KiB piece per wave per K-stage,
+  // kSub K-stages per ring slot
+  auto dma_gram = [&](int buf, int kt2) {
+    unroll<kSub>([&](auto h) {
+      constexpr int H = decltype(h)::value;
+      const char* src = reinterpret_cast<const char*>(x0 + (kSub * kt2 + H) * (kT * kBK)) + wave * 1024;
+      lds_dma16(src, lane16,
+                __builtin_amdgcn_readfirstlane(lds_addr(smem + kOffRing + buf * kSlot + H * kStage + wave * 64)));
+    });
   };
   // update stream position q = 4 j + kt: rows 32 kt .. of column tile j of X
-  auto dma_upd = [&](const T* xs, int buf, int q) {
-    const int j = q >> 2, kt = q & 3;
-    const int cb = wave >> 1, within = (wave & 1) * 1024;
-    const char* src = reinterpret_cast<const char*>(xs + ((4 * j + cb) * kT + 32 * kt) * kBK) + within;
-    lds_dma16(src, lane16, __builtin_amdgcn_readfirstlane(lds_addr(smem + kOffRing + buf * kStage + wave * 64)));
+  auto dma_upd = [&](const T* xs, int buf, int q2) {
+    unroll<kSub>([&](auto h) {
+      constexpr int H = decltype(h)::value;
+      const int q = kSub * q2 + H;
+      const int j = q >> 2, kt = q & 3;
+      const int cb = wave >> 1, within = (wave & 1) * 1024;
+      const char* src = reinterpret_cast<const char*>(xs + ((4 * j + cb) * kT + 32 * kt) * kBK) + within;
+      lds_dma16(src, lane16,
+                __builtin_amdgcn_readfirstlane(lds_addr(smem + kOffRing + buf * kSlot + H * kStage + wave * 64)));
+    });
   };
 
   // -------- S_0 = r^2 X_0 X_0^T
   zero(accs);
-  for (int s = 0; s < kNST; ++s) dma_gram(s, min(s, nkx - 1));
-  for (int kt = 0; kt < nkx; ++kt) {
-    const int cur = kt % kNST;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kNST - 1));     // stage kt landed (own piece)
-    barrier();                                            // ... and every wave's
-    const int base = kOffRing + cur * kStage;
-    unroll<2>([&](auto ks) {
-      const u32x4 fb = frag_nt(base, wc + l32, decltype(ks)::value);
-      unroll<2>([&](auto i) {
-        const u32x4 fa = frag_nt(base, wr + 32 * decltype(i)::value + l32, decltype(ks)::value);
-        accs[decltype(i)::value] = E::mma(fa, fb, accs[decltype(i)::value]);
+  const int nk2 = nkx / kSub;             // n_pad is a multiple of 128
+  for (int s = 0; s < kNST; ++s) dma_gram(s, min(s, nk2 - 1));
+  for (int kt2 = 0; kt2 < nk2; ++kt2) {
+    const int cur = kt2 % kNST;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNST - 1) * kSub));   // slot kt2 landed (own pieces)
+    barrier();                                                  // ... and every wave's
+    unroll<kSub>([&](auto h) {
+      const int base = kOffRing + cur * kSlot + decltype(h)::value * kStage;
+      unroll<2>([&](auto ks) {
+        const u32x4 fb = frag_nt(base, wc + l32, decltype(ks)::value);
+        unroll<2>([&](auto i) {
+          const u32x4 fa = frag_nt(base, wr + 32 * decltype(i)::value + l32, decltype(ks)::value);
+          accs[decltype(i)::value] = E::mma(fa, fb, accs[decltype(i)::value]);
+        });
       });
     });
-    lds_sync();                                           // stage kt fully read
-    dma_gram(cur, min(kt + kNST, nkx - 1));
+    lds_sync();                                                 // slot kt2 fully read
+    dma_gram(cur, min(kt2 + kNST, nk2 - 1));
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   store_nt(ls, accs, r0 * r0);
@@ -203,24 +222,27 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
 
     // -------- X_{k+1} = s P' X_k, column tile by column tile
     if (!last) zero(accs);
-    const int nq = 4 * ntj;
-    for (int q = 0; q < kNST; ++q) dma_upd(xs, q, min(q, nq - 1));
+    const int nq2 = 4 * ntj / kSub;
+    for (int q2 = 0; q2 < kNST; ++q2) dma_upd(xs, q2, min(q2, nq2 - 1));
     zero(acc);
-    for (int q = 0; q < nq; ++q) {
-      const int kt = q & 3, j = q >> 2, cur = q % kNST;
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kNST - 1));
+    for (int q2 = 0; q2 < nq2; ++q2) {
+      const int kt0 = (kSub * q2) & 3, j = (kSub * q2) >> 2, cur = q2 % kNST;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNST - 1) * kSub));
       barrier();
-      const int base = kOffRing + cur * kStage;
-      unroll<2>([&](auto ks) {
-        const u32x4 fb = frag_km(base, decltype(ks)::value);
-        unroll<2>([&](auto i) {
-          const u32x4 fa = frag_nt(kOffP + kt * kStage, wr + 32 * decltype(i)::value + l32, decltype(ks)::value);
-          acc[decltype(i)::value] = E::mma(fb, fa, acc[decltype(i)::value]);   // swapped: (row, 4 columns)
+      unroll<kSub>([&](auto h) {
+        const int base = kOffRing + cur * kSlot + decltype(h)::value * kStage;
+        const int kt = kt0 + decltype(h)::value;
+        unroll<2>([&](auto ks) {
+          const u32x4 fb = frag_km(base, decltype(ks)::value);
+          unroll<2>([&](auto i) {
+            const u32x4 fa = frag_nt(kOffP + kt * kStage, wr + 32 * decltype(i)::value + l32, decltype(ks)::value);
+            acc[decltype(i)::value] = E::mma(fb, fa, acc[decltype(i)::value]);   // swapped: (row, 4 columns)
+          });
         });
       });
       lds_sync();
-      dma_upd(xs, cur, min(q + kNST, nq - 1));
-      if (kt != 3) continue;
+      dma_upd(xs, cur, min(q2 + kNST, nq2 - 1));
+      if (kt0 + kSub != 4) continue;
 
       // tile j complete.  Swapped operands: register r of block i holds row
       // wr + 32 i + l32, column wc + 8 (r/4) + 4 lh + r%4 of the tile.
