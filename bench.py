@@ -170,8 +170,11 @@ def svd_main(args, torch, mo_amd, W, wl, dev):
         if n:
             unit = {"svd_gram": "TFLOP/s", "svd_eig": "Gpivot/s"}.get(c, "GB/s")
             scale = {"TFLOP/s": 1e12, "Gpivot/s": 1e9, "GB/s": 1e9}[unit]
+            rate = work / (ms * 1e-3) / scale if ms > 0 else None
+            pk = {"TFLOP/s": FP64_PEAK_TFLOPS, "GB/s": HBM_PEAK_GBS}.get(unit)
             kernels[c] = {"launches": n, "ms_per_run": ms / args.steps, "mean_ms": ms / n,
-                          "rate": work / (ms * 1e-3) / scale if ms > 0 else None, "unit": unit}
+                          "rate": rate, "unit": unit,
+                          "frac": rate / pk if (rate is not None and pk) else None}
     red = prof["svd_reduce"]
     roofline = None
     if red[0]:
@@ -282,7 +285,8 @@ def main():
         if n:
             unit = "TFLOP/s" if c in ("gram", "poly", "update", "apply") else "GB/s"
             rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-            kernels[c] = {"launches": n, "mean_ms": ms / n, "rate": rate, "unit": unit}
+            kernels[c] = {"launches": n, "mean_ms": ms / n, "rate": rate, "unit": unit,
+                          "frac": rate / (peak if unit == "TFLOP/s" else HBM_PEAK_GBS)}
     upd = prof["update"]
     roofline = None
     if upd[0]:

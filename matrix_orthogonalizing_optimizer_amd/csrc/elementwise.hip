@@ -109,17 +109,83 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// kW = 8 consecutive elements of one row: 16 bytes of bf16, or two
+// 16-byte halves of fp32 (each half one vector access when aligned).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+template <int kW, bool kNT>
+__device__ __forceinline__ void loadw(const void* base, int dt, int64_t off, int nvalid, bool vecw,
+                                      bool vec4, float v[kW]) {
+  if (kW == 8 && dt == BF16 && vecw) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    u32x4v q;
+    if constexpr (kNT) q = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    else q = *reinterpret_cast<const u32x4v*>(p);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[2 * h] = bf2f(q[h] & 0xffffu);
+      v[2 * h + 1] = bf2f(q[h] >> 16);
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < kW / 4; ++h) {
+    const int nv = max(0, min(4, nvalid - 4 * h));
+    load4<kNT>(base, dt, off + 4 * h, nv, vec4 && nv == 4, v + 4 * h);
+  }
+}
+
+template <int kW, bool kNT>
+__device__ __forceinline__ void storew(void* base, int dt, int64_t off, int nvalid, bool vecw,
+                                       bool vec4, const float v[kW]) {
+  if (kW == 8 && dt == BF16 && vecw) {
+    uint16_t* p = static_cast<uint16_t*>(base) + off;
+    u32x4v q;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      q[h] = static_cast<uint32_t>(f2bf(v[2 * h])) | (static_cast<uint32_t>(f2bf(v[2 * h + 1])) << 16);
+    if constexpr (kNT) __builtin_nontemporal_store(q, reinterpret_cast<u32x4v*>(p));
+    else *reinterpret_cast<u32x4v*>(p) = q;
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < kW / 4; ++h) {
+    const int nv = max(0, min(4, nvalid - 4 * h));
+    store4<kNT>(base, dt, off + 4 * h, nv, vec4 && nv == 4, v + 4 * h);
+  }
+}
+
+// kW consecutive elements of X (oriented row xr, columns xc ..) in the
+// blocked layout: a 16-byte chunk holds 8 bf16 or 4 fp32 consecutive
+// columns, so a bf16 group of 8 is one store and an fp32 group one store
+// per 4 (chunks are permuted within a row).
+template <int kW>
+__device__ __forceinline__ void store_x(char* x, int ns_dt, const Blocked& Lx, int xr, int xc,
+                                        const float v[kW]) {
+  if (kW == 8 && ns_dt == BF16) {
+    storew<kW, false>(x, ns_dt, blk_off(Lx, xr, xc), kW, true, true, v);
+  } else {
+#pragma unroll
+    for (int h = 0; h < kW / 4; ++h) store4(x, ns_dt, blk_off(Lx, xr, xc + 4 * h), 4, true, v + 4 * h);
+  }
+}
+
 // One 64x64 tile of the padded natural domain [A_pad, B_pad] per block.
-// Thread layout: 16 threads x 4 columns across a row, 16 rows per pass.
-// The Newton-Schulz input is written once, in the oriented layout
-// [m_pad, n_pad]: straight through for a wide parameter, transposed through
-// an LDS tile for a tall one (its columns are the rows of X).
-// kAhead: every load of the thread's four rows is issued before any
-// arithmetic or store (the momentum stores may alias later rows' loads, so
-// the compiler would not hoist them by itself).  It pays for 8-byte (bf16)
-// gradient loads; with 16-byte fp32 loads the row-by-row order is as fast.
-template <bool kAhead>
+// Thread layout: 64 / kW threads x kW columns across a row, 256 / (64 / kW)
+// rows per pass.  The Newton-Schulz input is written once, in the oriented
+// layout [m_pad, n_pad]: straight through for a wide parameter, transposed
+// through an LDS tile for a tall one (its columns are the rows of X).
+// kW = 8 serves bf16 gradients: 16-byte accesses for the bf16 arrays, and
+// every load of the thread's rows issued before any arithmetic or store
+// (the momentum stores may alias later rows' loads, so the compiler would
+// not hoist them by itself).  kW = 4 serves fp32 gradients, whose 16-byte
+// loads run as fast row by row.
+template <int kW>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
+  constexpr int kTX = 64 / kW;           // threads across a row
+  constexpr int kRows = 256 / kTX;       // rows per pass
+  constexpr int kPasses = 64 / kRows;
+  constexpr bool kAhead = kW == 8;
   __shared__ float tile[64][65];
   __shared__ float red[4];
   const int b = blockIdx.x / p.tiles_per_mat;
@@ -130,77 +196,78 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   const int B_pad = ori ? p.m_pad : p.n_pad;
   const int tiles_b = B_pad >> 6;
   const int ta = t / tiles_b, tb = t - ta * tiles_b;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int tx = threadIdx.x % kTX, ty = threadIdx.x / kTX;
   const int esz = p.ns_dt == F32 ? 4 : 2;
   char* x = static_cast<char*>(p.x) + b * p.x_stride * esz;
   const Blocked Lx = blocked(p.tile, p.n_pad, esz);      // X: [m_pad, n_pad]
-  const bool vec_ok = (B & 3) == 0;
+  const bool vec4 = (B & 3) == 0;
+  const bool vecw = (B % kW) == 0;
   float sq = 0.0f;
 
-  const int c = tb * 64 + tx * 4;
-  const int nvalid = max(0, min(4, B - c));
-  float g[4][4], m[4][4];
+  const int c = tb * 64 + tx * kW;
+  const int nvalid = max(0, min(kW, B - c));
+  const bool full = vecw && nvalid == kW;
+  float g[kPasses][kW], m[kPasses][kW];
   if constexpr (kAhead) {
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int r = ta * 64 + ty + pass * 16;
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int r = ta * 64 + ty + pass * kRows;
       if (r < A && nvalid > 0) {
         const int64_t off = static_cast<int64_t>(r) * B + c;
-        const bool vec = vec_ok && nvalid == 4;
-        load4<true>(md.grad, p.grad_dt, off, nvalid, vec, g[pass]);
-        if (p.has_mom) load4<true>(md.mom, p.mom_dt, off, nvalid, vec, m[pass]);
+        loadw<kW, true>(md.grad, p.grad_dt, off, nvalid, full, vec4, g[pass]);
+        if (p.has_mom) loadw<kW, true>(md.mom, p.mom_dt, off, nvalid, full, vec4, m[pass]);
       }
     }
   }
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int rl = ty + pass * 16;
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int rl = ty + pass * kRows;
     const int r = ta * 64 + rl;
-    float n4[4] = {0.f, 0.f, 0.f, 0.f};
+    float n4[kW];
+#pragma unroll
+    for (int j = 0; j < kW; ++j) n4[j] = 0.0f;
     if (r < A && nvalid > 0) {
       const int64_t off = static_cast<int64_t>(r) * B + c;
-      const bool vec = vec_ok && nvalid == 4;
       if constexpr (!kAhead) {
-        load4<true>(md.grad, p.grad_dt, off, nvalid, vec, g[pass]);
-        if (p.has_mom) load4<true>(md.mom, p.mom_dt, off, nvalid, vec, m[pass]);
+        loadw<kW, true>(md.grad, p.grad_dt, off, nvalid, full, vec4, g[pass]);
+        if (p.has_mom) loadw<kW, true>(md.mom, p.mom_dt, off, nvalid, full, vec4, m[pass]);
       }
       if (p.has_mom) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kW; ++j) {
           const float mn = p.mu * m[pass][j] + g[pass][j];
           m[pass][j] = mn;
           n4[j] = p.nesterov ? p.mu * mn + g[pass][j] : mn;
         }
-        store4<true>(md.mom, p.mom_dt, off, nvalid, vec, m[pass]);
+        storew<kW, true>(md.mom, p.mom_dt, off, nvalid, full, vec4, m[pass]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) n4[j] = g[pass][j];
+        for (int j = 0; j < kW; ++j) n4[j] = g[pass][j];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kW; ++j) {
         if (j >= nvalid) n4[j] = 0.0f;
         sq += n4[j] * n4[j];
       }
     }
     if (!ori) {
-      // padding written as zeros; 4 consecutive columns stay inside one
-      // 16-byte chunk of the blocked layout
-      store4(x, p.ns_dt, blk_off(Lx, r, c), 4, true, n4);
+      // padding written as zeros
+      store_x<kW>(x, p.ns_dt, Lx, r, c, n4);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tile[rl][tx * 4 + j] = n4[j];
+      for (int j = 0; j < kW; ++j) tile[rl][tx * kW + j] = n4[j];
     }
   }
   if (ori) {
     __syncthreads();
     // rows of X are columns of the tile
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int cl = ty + pass * 16;
-      float v[4];
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int cl = ty + pass * kRows;
+      float v[kW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = tile[tx * 4 + j][cl];
-      store4(x, p.ns_dt, blk_off(Lx, tb * 64 + cl, ta * 64 + tx * 4), 4, true, v);
+      for (int j = 0; j < kW; ++j) v[j] = tile[tx * kW + j][cl];
+      store_x<kW>(x, p.ns_dt, Lx, tb * 64 + cl, ta * 64 + tx * kW, v);
     }
   }
   const float s = block_sum_256(sq, red);
@@ -338,8 +405,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
 }
 
 hipError_t launch_prep(const PrepArgs& a, int chunk, hipStream_t s) {
-  if (a.grad_dt == BF16) hipLaunchKernelGGL(prep_kernel<true>, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(prep_kernel<false>, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
+  if (a.grad_dt == BF16) hipLaunchKernelGGL(prep_kernel<8>, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(prep_kernel<4>, dim3(a.tiles_per_mat * chunk), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 hipError_t launch_norm(const NormArgs& a, int chunk, hipStream_t s) {

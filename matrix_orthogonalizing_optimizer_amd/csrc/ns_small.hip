@@ -33,6 +33,7 @@ constexpr int kNT = 512;                // threads
 constexpr int kStage = kT * kCPR;       // chunks of one [128 rows][64 B] stage (8 KiB)
 constexpr int kSub = 2;                 // K-stages per ring slot (one barrier pair per slot)
 constexpr int kSlot = kSub * kStage;
+static_assert(4 % kSub == 0, "a 128-column tile's 4 K-stages fill whole slots");
 constexpr int kNST = 2;                 // ring slots
 // LDS map in 16-byte chunks.  P', S and the X' tile are [4 K-stages][128
 // rows][64 B] (chunks permuted per row as in global memory); a ring slot

@@ -37,6 +37,9 @@ def _check_common(d, steps, warmup):
     assert ROOF <= set(roof), ROOF - set(roof)
     assert 0 < roof["frac"] < 1 and abs(roof["achieved"] / roof["peak"] - roof["frac"]) < 1e-9
     assert roof["traffic"] is None or roof["traffic"] > 0
+    for name, k in d["kernels"].items():
+        if k["unit"] in ("TFLOP/s", "GB/s"):
+            assert 0 < k["frac"] < 1 and k["rate"] > 0, (name, k)
 
 
 def test_bench_default_line():
