@@ -42,6 +42,16 @@
  *            MO_EHIP).  NaN and Inf propagate per IEEE arithmetic.
  *   Threads  Entry points are thread-safe except that a plan must not be
  *            stepped from two threads at once.
+ *   Tuning   Environment switches for tests and measurement only (MO_TILE
+ *            is read when matrices are binned, i.e. at plan creation or per
+ *            one-shot call; the others at launch); results stay within the
+ *            same tolerances:
+ *              MO_TILE=64|128|256  force the output tile of every shape
+ *                                  group (256: bf16 only);
+ *              MO_WAVES=4|8        waves per 256-tile workgroup (default 8);
+ *              MO_NO_SMALL=1       run groups of small matrices (m <= 128)
+ *                                  through the per-product kernels instead
+ *                                  of the fused one.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H
