@@ -34,7 +34,7 @@ constexpr int kStage = kT * kCPR;       // chunks of one [128 rows][64 B] stage 
 constexpr int kSub = 2;                 // K-stages per ring slot (one barrier pair per slot)
 constexpr int kSlot = kSub * kStage;
 static_assert(4 % kSub == 0, "a 128-column tile's 4 K-stages fill whole slots");
-constexpr int kNST = 2;                 // ring slots
+constexpr int kNST = 3;                 // ring slots (two in flight)
 // LDS map in 16-byte chunks.  P', S and the X' tile are [4 K-stages][128
 // rows][64 B] (chunks permuted per row as in global memory); a ring slot
 // holds kSub Gram stages [128 rows][64 B] or kSub update blocks [4 column
@@ -178,11 +178,20 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
   // -------- S_0 = r^2 X_0 X_0^T
   zero(accs);
   const int nk2 = nkx / kSub;             // n_pad is a multiple of 128
-  for (int s = 0; s < kNST; ++s) dma_gram(s, min(s, nk2 - 1));
+  // One barrier per slot: before it a wave waits until its own pieces of
+  // slot kt2 have landed (the next kNST - 2 slots may still be in flight)
+  // and its LDS reads are done; after it every wave's part of slot kt2 is
+  // visible and slot kt2 - 1 has been fully read, so its buffer takes slot
+  // kt2 + kNST - 1.  Past the end the last slot is loaded again, so the
+  // number of loads in flight is the same at every wait.
+  auto prev = [](int cur) { return cur == 0 ? kNST - 1 : cur - 1; };
+  for (int s = 0; s < kNST - 1; ++s) dma_gram(s, min(s, nk2 - 1));
   for (int kt2 = 0; kt2 < nk2; ++kt2) {
     const int cur = kt2 % kNST;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNST - 1) * kSub));   // slot kt2 landed (own pieces)
-    barrier();                                                  // ... and every wave's
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNST - 2) * kSub));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
+    dma_gram(prev(cur), min(kt2 + kNST - 1, nk2 - 1));
     unroll<kSub>([&](auto h) {
       const int base = kOffRing + cur * kSlot + decltype(h)::value * kStage;
       unroll<2>([&](auto ks) {
@@ -193,8 +202,6 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
         });
       });
     });
-    lds_sync();                                                 // slot kt2 fully read
-    dma_gram(cur, min(kt2 + kNST, nk2 - 1));
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   store_nt(ls, accs, r0 * r0);
@@ -224,12 +231,14 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
     // -------- X_{k+1} = s P' X_k, column tile by column tile
     if (!last) zero(accs);
     const int nq2 = 4 * ntj / kSub;
-    for (int q2 = 0; q2 < kNST; ++q2) dma_upd(xs, q2, min(q2, nq2 - 1));
+    for (int q2 = 0; q2 < kNST - 1; ++q2) dma_upd(xs, q2, min(q2, nq2 - 1));
     zero(acc);
     for (int q2 = 0; q2 < nq2; ++q2) {
       const int kt0 = (kSub * q2) & 3, j = (kSub * q2) >> 2, cur = q2 % kNST;
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNST - 1) * kSub));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNST - 2) * kSub));   // as in the Gram loop
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       barrier();
+      dma_upd(xs, prev(cur), min(q2 + kNST - 1, nq2 - 1));
       unroll<kSub>([&](auto h) {
         const int base = kOffRing + cur * kSlot + decltype(h)::value * kStage;
         const int kt = kt0 + decltype(h)::value;
@@ -241,8 +250,6 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
           });
         });
       });
-      lds_sync();
-      dma_upd(xs, cur, min(q2 + kNST, nq2 - 1));
       if (kt0 + kSub != 4) continue;
 
       // tile j complete.  Swapped operands: register r of block i holds row
