@@ -446,7 +446,9 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
         gb.D = it.S; gb.sD = it.L.s_elems;
         gb.C = it.P; gb.sC = it.L.s_elems;
         gb.M = bin.m_pad; gb.N = bin.m_pad; gb.K = bin.m_pad;
-        gb.k_loop = gb.K / bk;
+        // K runs over S's columns: stages past the true m multiply its zero
+        // padding only
+        gb.k_loop = (bin.m + bk - 1) / bk;
         gb.tiles_m = tm; gb.tiles_n = tm; gb.tiles_per_mat = tm * (tm + 1) / 2;
         work += it.chunk * m * m * m;
       } else {                          // X' = P' X, X read K-major from its own layout

@@ -452,10 +452,13 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   } else {
     // the FMM capture stages unrolled, so every accumulator index is a
     // compile-time constant
-    run_range(0, cap_kt);
+    // With K trimmed to the true m, capture stages at or past nkl hold
+    // only S's zero padding and are skipped; every wave still runs exactly
+    // nkl iterations (one barrier each), so the barriers stay matched.
+    run_range(0, min(cap_kt, nkl));
     unroll<FMM>([&](auto i) {
       const int kt = cap_kt + decltype(i)::value;
-      iteration(kt, i, kt % NST);
+      if (kt < nkl) iteration(kt, i, kt % NST);
     });
     run_range(cap_kt + FMM, nkl);
   }
@@ -758,25 +761,34 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     constexpr int kGroups = kPR * TILE / 4;                 // groups per pass
     constexpr int kU = kGroups >= NT * 8 ? 8 : kGroups / NT;
     static_assert(kU >= 1 && kGroups % (NT * kU) == 0, "group loop");
-    // whole tile inside the parameter, rows a multiple of 4: all of a step's
-    // loads (LDS x, W) are issued before any store
+    // Row length a multiple of 4: every group of four lies wholly inside or
+    // wholly outside the parameter, so groups go as 16-byte accesses.  A
+    // tile inside the parameter needs no check (guard false); a ragged one
+    // skips the groups outside.  All of a step's loads (LDS x, W) are
+    // issued before any store.
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(1))) f32x4_t gf4;
-    auto copy_full = [&](auto pc, auto oric) {
+    auto copy_full = [&](auto pc, auto oric, auto guardc) {
+      constexpr bool kGuard = decltype(guardc)::value;
 #pragma unroll 1
       for (int g0 = 0; g0 < kGroups; g0 += NT * kU) {
         f32x4_t xv[kU], wv[kU];
         int64_t off[kU];
+        bool in[kU];
         unroll<kU>([&](auto u) {
           constexpr int U = decltype(u)::value;
           int wrow, wcol;
           const int lo = group(pc, oric, g0 + U * NT + tid, wrow, wcol);
+          in[U] = !kGuard || (wrow < wrows && wcol < ldw);
           off[U] = static_cast<int64_t>(wrow) * ldw + wcol;
           xv[U] = *reinterpret_cast<const f32x4_t*>(lf + lo);
-          if constexpr (EPI == EPI_APPLY) wv[U] = *(const gf4*)(W + off[U]);
+          if constexpr (EPI == EPI_APPLY) {
+            if (in[U]) wv[U] = *(const gf4*)(W + off[U]);
+          }
         });
         unroll<kU>([&](auto u) {
           constexpr int U = decltype(u)::value;
+          if (!in[U]) return;
           const f32x4_t x = xv[U];
           if constexpr (EPI == EPI_APPLY) {
             const f32x4_t w = wv[U];
@@ -788,7 +800,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
         });
       }
     };
-    // ragged tile or row length not a multiple of 4: element by element
+    // row length not a multiple of 4: element by element
     auto copy_edge = [&](auto pc, auto oric) {
 #pragma unroll 1
       for (int g = tid; g < kGroups; g += NT) {
@@ -818,7 +830,8 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
         if (wr / kPR == decltype(pc)::value) stage(pc, oric);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         barrier();
-        if (full) copy_full(pc, oric);
+        if (full) copy_full(pc, oric, False{});
+        else if ((ldw % 4) == 0) copy_full(pc, oric, True{});
         else copy_edge(pc, oric);
       });
     };
