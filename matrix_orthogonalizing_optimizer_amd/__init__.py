@@ -392,10 +392,16 @@ class MuonAdamW:
                 "exp_avg_sq": [v.clone() for v in self.exp_avg_sq]}
 
     def load_state_dict(self, sd: dict) -> None:
+        # checked in full before anything is copied
+        for name in ("momentum", "exp_avg", "exp_avg_sq"):
+            dst, src = getattr(self, name), sd[name]
+            if len(src) != len(dst):
+                raise ValueError(f"state_dict[{name!r}] has {len(src)} tensors, the optimizer {len(dst)}")
+            for i, (d, t) in enumerate(zip(dst, src)):
+                if tuple(t.shape) != tuple(d.shape):
+                    raise ValueError(f"state_dict[{name!r}][{i}] has shape {tuple(t.shape)}, "
+                                     f"expected {tuple(d.shape)}")
         self.t = int(sd["t"])
-        for dst, src in zip(self.momentum, sd["momentum"]):
-            dst.copy_(src)
-        for dst, src in zip(self.exp_avg, sd["exp_avg"]):
-            dst.copy_(src)
-        for dst, src in zip(self.exp_avg_sq, sd["exp_avg_sq"]):
-            dst.copy_(src)
+        for name in ("momentum", "exp_avg", "exp_avg_sq"):
+            for d, t in zip(getattr(self, name), sd[name]):
+                d.copy_(t)
