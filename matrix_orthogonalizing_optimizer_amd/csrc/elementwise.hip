@@ -158,15 +158,17 @@ __device__ __forceinline__ void storew(void* base, int dt, int64_t off, int nval
 // kW consecutive elements of X (oriented row xr, columns xc ..) in the
 // blocked layout: a 16-byte chunk holds 8 bf16 or 4 fp32 consecutive
 // columns, so a bf16 group of 8 is one store and an fp32 group one store
-// per 4 (chunks are permuted within a row).
+// per 4 (chunks are permuted within a row).  Non-temporal like the other
+// streams: X of a whole step is far larger than the caches, so the first
+// Gram reads it from HBM either way.
 template <int kW>
 __device__ __forceinline__ void store_x(char* x, int ns_dt, const Blocked& Lx, int xr, int xc,
                                         const float v[kW]) {
   if (kW == 8 && ns_dt == BF16) {
-    storew<kW, false>(x, ns_dt, blk_off(Lx, xr, xc), kW, true, true, v);
+    storew<kW, true>(x, ns_dt, blk_off(Lx, xr, xc), kW, true, true, v);
   } else {
 #pragma unroll
-    for (int h = 0; h < kW / 4; ++h) store4(x, ns_dt, blk_off(Lx, xr, xc + 4 * h), 4, true, v + 4 * h);
+    for (int h = 0; h < kW / 4; ++h) store4<true>(x, ns_dt, blk_off(Lx, xr, xc + 4 * h), 4, true, v + 4 * h);
   }
 }
 
