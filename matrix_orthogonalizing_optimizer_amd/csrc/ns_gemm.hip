@@ -491,7 +491,10 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
   static_assert(kApply || kSmemChunks * 16 >= TILE * TILE * static_cast<int>(sizeof(T)), "tile staging");
   constexpr int kTileChunks = TILE * TILE * static_cast<int>(sizeof(T)) / 16;
   // LDS tile -> contiguous global range: 16 bytes per thread and step, eight
-  // steps' loads in flight before their stores
+  // steps' loads in flight before their stores.  The stores are
+  // non-temporal: the next product reads the output after every tile of
+  // this one is written, and a whole output is larger than the caches, so
+  // keeping it would only evict operand panels other tiles still read.
   auto copy_out = [&](T* dst) {
     u32x4* g = reinterpret_cast<u32x4*>(dst);
     constexpr int kIter = kTileChunks / NT;
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(64 * NW) void ns_gemm_kernel(GemmArgs p) {
     for (int c0 = 0; c0 < kIter; c0 += kB) {
       u32x4 v[kB];
       unroll<kB>([&](auto k) { v[decltype(k)::value] = smem[tid + (c0 + decltype(k)::value) * NT]; });
-      unroll<kB>([&](auto k) { g[tid + (c0 + decltype(k)::value) * NT] = v[decltype(k)::value]; });
+      unroll<kB>([&](auto k) { __builtin_nontemporal_store(v[decltype(k)::value], &g[tid + (c0 + decltype(k)::value) * NT]); });
     }
   };
 
