@@ -421,7 +421,11 @@ __global__ __launch_bounds__(256) void svd_trd_pass_kernel(SvdTrdArgs p, int j, 
 
   double x[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) x[q] = a[static_cast<int64_t>(min(g.rbase + q, m - 1)) * m + g.colc];
+  // non-temporal: a step streams the whole trailing block, which is far
+  // larger than the caches, and keeping it would evict the slots the
+  // column kernel reads next
+  for (int q = 0; q < 16; ++q)
+    x[q] = __builtin_nontemporal_load(&a[static_cast<int64_t>(min(g.rbase + q, m - 1)) * m + g.colc]);
   const double vnc = vn[g.colc];
   const double rv = g.tc < 16 ? vn[min(g.rbase + g.tc, m - 1)] : 0.0;
   double cp = 0.0;
@@ -493,7 +497,8 @@ __global__ __launch_bounds__(256) void svd_trd_panel_kernel(SvdTrdArgs p, int r0
 
   double x[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) x[q] = a[static_cast<int64_t>(min(g.rbase + q, m - 1)) * m + g.colc];
+  for (int q = 0; q < 16; ++q)   // non-temporal, as in the pass kernel
+    x[q] = __builtin_nontemporal_load(&a[static_cast<int64_t>(min(g.rbase + q, m - 1)) * m + g.colc]);
   double cv[kP], cw[kP];
 #pragma unroll
   for (int t = 0; t < kP; ++t) {
