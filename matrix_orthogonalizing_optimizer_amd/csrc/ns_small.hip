@@ -306,13 +306,16 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
           const float* xv = lf + rr * kApLd + c4;
           float* wp = W + (row0 + rr) * ldw + col0 + c4;
           if (full) {
-            float4 w = *reinterpret_cast<const float4*>(wp);
+            // W is read and written once per step: non-temporal (unlike X,
+            // which this workgroup reads back in the next iteration)
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            f4v w = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(wp));
             const float4 x = *reinterpret_cast<const float4*>(xv);
-            w.x -= p.lrwd * w.x + g.step * x.x;
-            w.y -= p.lrwd * w.y + g.step * x.y;
-            w.z -= p.lrwd * w.z + g.step * x.z;
-            w.w -= p.lrwd * w.w + g.step * x.w;
-            *reinterpret_cast<float4*>(wp) = w;
+            w[0] -= p.lrwd * w[0] + g.step * x.x;
+            w[1] -= p.lrwd * w[1] + g.step * x.y;
+            w[2] -= p.lrwd * w[2] + g.step * x.z;
+            w[3] -= p.lrwd * w[3] + g.step * x.w;
+            __builtin_nontemporal_store(w, reinterpret_cast<f4v*>(wp));
             sq += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
           } else {
             for (int e = 0; e < 4 && c4 + e < wcols; ++e) {
