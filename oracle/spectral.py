@@ -65,6 +65,84 @@ def per_sigma_deviation(X, N, steps: int = NS_STEPS, abc=NS_COEFFS,
     return float(np.max(np.abs(proj - target))) if s.size else 0.0
 
 
+def short_side_eig(N):
+    """Singular values and short-side singular vectors of ``N`` from the
+    symmetric eigenproblem of its short-side Gram matrix.
+
+    For ``N [A, B]`` with ``A <= B``: ``N N^T = U diag(sigma^2) U^T``, so the
+    eigenvectors are the left singular vectors; for ``A > B`` the Gram matrix
+    is ``N^T N`` and they are the right singular vectors.  Eigenvalues that
+    rounding pushed below zero are clipped.  Returns ``(sigma, Q, tall)``
+    with ``sigma`` largest first and ``Q``'s columns the matching vectors.
+    This is the same factorisation as the thin SVD (an identity, not an
+    approximation) at the cost of one product and one eigensolve, which is
+    what makes 8192-class matrices affordable in fp64.
+    """
+    N = np.asarray(N, dtype=np.float64)
+    tall = N.shape[0] > N.shape[1]
+    G = N.T @ N if tall else N @ N.T
+    lam, Q = np.linalg.eigh(G)
+    order = np.argsort(lam)[::-1]
+    lam, Q = lam[order], Q[:, order]
+    return np.sqrt(np.maximum(lam, 0.0)), Q, tall
+
+
+def _map_over_x(y_over, x, steps, abc):
+    """``f^N(x) / x`` elementwise, with its limit ``a^N`` at ``x = 0``."""
+    a = float(abc[0])
+    out = np.full_like(x, a ** int(steps))
+    nz = x > 0.0
+    out[nz] = y_over(x[nz]) / x[nz]
+    return out
+
+
+def ns_closed_form_gram(N, steps: int = NS_STEPS, abc=NS_COEFFS,
+                        eps: float = NORM_EPS):
+    """The closed form of ``ns_closed_form`` taken through ``short_side_eig``.
+
+    ``U f^N(S / nu) V^T = U diag(f^N(sigma_i / nu) / sigma_i) U^T N`` (wide;
+    ``N Q diag(.) Q^T`` when tall), since ``V^T = S^{-1} U^T N``.  The ratio
+    ``f^N(x) / x`` is smooth down to ``x = 0`` (limit ``a^N``), so directions
+    with tiny or zero singular values need no special care.
+    """
+    N = np.asarray(N, dtype=np.float64)
+    sigma, Q, tall = short_side_eig(N)
+    nu = float(np.sqrt(np.sum(N * N)))
+    x = sigma / (nu + eps)
+    h = _map_over_x(lambda t: scalar_map(t, steps, abc), x, steps, abc) / (nu + eps)
+    K = (Q * h) @ Q.T
+    return N @ K if tall else K @ N
+
+
+def per_sigma_deviation_gram(X, N, steps: int = NS_STEPS, abc=NS_COEFFS,
+                             eps: float = NORM_EPS, rel_floor: float = 0.0) -> float:
+    """``per_sigma_deviation`` with the singular triplets of ``N`` from
+    ``short_side_eig``.
+
+    With ``u_i`` a short-side singular vector and ``sigma_i > 0``, the
+    long-side partner is ``v_i = N^T u_i / sigma_i`` (wide), so
+    ``u_i^T X v_i = u_i^T (X N^T) u_i / sigma_i`` and only one product with
+    ``N`` is needed.  Directions with ``sigma_i <= rel_floor * sigma_1`` (and
+    exact zeros, whose partner is undefined) are left out; the Gram matrix
+    returns exact zeros of N as singular values near ``1e-8 sigma_1``, so a
+    rank-deficient input needs a floor above that.
+    """
+    N = np.asarray(N, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    if N.shape != X.shape:
+        raise ValueError("X and N must have the same shape")
+    sigma, Q, tall = short_side_eig(N)
+    nu = float(np.sqrt(np.sum(N * N)))
+    target = scalar_map(sigma / (nu + eps), steps, abc)
+    B = X.T @ N if tall else X @ N.T               # short x short
+    keep = sigma > max(rel_floor * (sigma[0] if sigma.size else 0.0), 0.0)
+    if not np.any(keep):
+        return 0.0
+    Qk = Q[:, keep]
+    proj = np.einsum("ij,ij->j", Qk, B @ Qk) / sigma[keep]
+    return float(np.max(np.abs(proj - target[keep])))
+
+
 def rel_fro(x, ref) -> float:
     """Relative Frobenius error ``||x - ref||_F / ||ref||_F`` (0/0 -> 0)."""
     x = np.asarray(x, dtype=np.float64)
