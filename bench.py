@@ -1,11 +1,12 @@
 """Benchmark of the Muon optimizer step on one MI355X.
 
-Default workload: the 800M-style dense decoder's full optimizer step --
-144 Muon matrices (24 layers x q/k/v/o [1536,1536] + MLP [1536,6144] and
-[6144,1536]; fp32 weights, fp32 gradients, bf16 momentum, bf16
-Newton-Schulz, N = 5) plus AdamW on 49 RMSNorm gains [1536] and an untied
-embedding and LM head [32000,1536].  Inputs are synthetic (seeded) and
-resident in HBM before timing starts.
+Default workload: the large-matrix step, the largest configuration that
+fits one GPU -- 16 x [8192,8192], 16 x [8192,28672] and 16 x [28672,8192]
+Muon matrices (fp32 weights, bf16 gradients, bf16 momentum, bf16
+Newton-Schulz, N = 5).  ``--workload`` selects the others (the 800M-style
+dense decoder with its AdamW side tensors, the 1.5B GQA model, the MoE
+share, the per-head split, N = 10, the fp32 matrix).  Inputs are synthetic
+(seeded) and resident in HBM before timing starts.
 
 One JSON line is printed.  `value` is optimizer steps/s over the timed
 steps (wall clock, synchronised on both sides).  The `roofline` object is
@@ -13,8 +14,12 @@ for the dominant kernel (the Newton-Schulz update GEMM X <- aX + PX): its
 algorithmic flops per launch divided by its mean launch time, measured with
 HIP events on the launch stream over the same timed steps.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload (one matrix per shape group, one tensor per AdamW group) and scales
-it to the whole step by the group counts.
+workload -- one matrix of every shape group (the whole N-iteration step, or,
+where that would take more than a few seconds, the step at N = 0 and N = 1,
+extrapolated linearly to N) and one tensor per AdamW group -- and scales it
+to the whole step by the group counts.  The roofline peaks are the
+datasheet's; the line also carries the peaks measured on the GPU by the
+probes of ``include/mo_probe.h`` (matrix cores alone, HBM streams alone).
 """
 
 from __future__ import annotations
@@ -71,12 +76,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dense800m",
-                    help="dense800m (default), llama1p5b_gqa, moe_share, large_n5, "
-                         "large_n10, fp32_128x512, kv_heads")
+    ap.add_argument("--workload", default="large_n5",
+                    help="large_n5 (default), large_n10, dense800m, llama1p5b_gqa, moe_share, "
+                         "fp32_128x512, kv_heads")
     ap.add_argument("--scaling", default="shape", choices=["shape", "hidden", "update_norm"],
                     help="update scaling: 0.2 sqrt(max(A,B)) (default), 0.2 sqrt(H) with H the "
-                         "largest matrix dimension, or 0.2 / RMS(X_N)")
+                         "workload model's hidden size, or 0.2 / RMS(X_N)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="do not measure the matrix-core and HBM peaks")
     ap.add_argument("--svd-entropy", action="store_true",
                     help="time the SVD-entropy diagnostic (section 3.4) over the workload's "
                          "Muon weight matrices instead of the optimizer step")
@@ -86,32 +93,54 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, muon_T, adam_T, budget_s: float = 30.0):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, muon_T, adam_T, direct_flops: float = 3e12):
     """Time the fp64 oracle on one matrix per shape group (and one tensor per
-    AdamW group), scale by the group counts; returns the baseline dict."""
-    import numpy as np
+    AdamW group), scale by the group counts; returns the baseline dict.
+
+    A group whose N-iteration oracle step exceeds ``direct_flops`` (dense
+    count) is timed at N = 0 and N = 1 and extrapolated linearly to N: the
+    iterations are identical, so the step costs t(0) + N (t(1) - t(0))."""
     from threadpoolctl import threadpool_info
 
     from oracle import muon_oracle as mo
 
+    import workloads as W
+
     def f64(t):
         return t.detach().float().cpu().double().numpy()
+
+    def timed(P, G, M, steps):
+        t0 = time.perf_counter()
+        mo.muon_step(P, G, M, ns_steps=steps, abc=mo.NS_COEFFS, **HYPER)
+        return time.perf_counter() - t0
 
     t_total = 0.0
     sample = []
     idx = 0
-    spent = 0.0
     for grp in wl.mats:
         P, G, M = (f64(x[idx]) for x in (muon_T.params, muon_T.grads, muon_T.moms))
-        t0 = time.perf_counter()
-        mo.muon_step(P, G, M, ns_steps=wl.ns_steps, abc=mo.NS_COEFFS, **HYPER)
-        dt = time.perf_counter() - t0
-        spent += dt
+        _, dense = W.ns_flops(grp.rows, grp.cols, wl.ns_steps)
+        if dense <= direct_flops:
+            dt = timed(P, G, M, wl.ns_steps)
+            sample.append(f"1 of {grp.count} [{grp.rows},{grp.cols}] ({dt:.2f} s)")
+        else:
+            t0 = timed(P, G, M, 0)
+            t1 = timed(P, G, M, 1)
+            dt = t0 + wl.ns_steps * max(t1 - t0, 0.0)
+            sample.append(f"1 of {grp.count} [{grp.rows},{grp.cols}] at N=0 ({t0:.2f} s) and N=1 "
+                          f"({t1:.2f} s), extrapolated to N={wl.ns_steps} ({dt:.1f} s)")
         t_total += dt * grp.count
-        sample.append(f"1 of {grp.count} [{grp.rows},{grp.cols}] ({dt:.2f} s)")
         idx += grp.count
-        if spent > budget_s:
-            break
     if adam_T is not None:
         k = 0
         for vg in wl.vecs:
@@ -124,9 +153,31 @@ def cpu_baseline(wl, muon_T, adam_T, budget_s: float = 30.0):
             k += vg.count
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     return {"value": 1.0 / t_total, "unit": "steps/s", "cores": threads,
-            "kind": "oracle",
-            "sample": ("fp64 numpy oracle, full step extrapolated from " + "; ".join(sample)
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": ("fp64 numpy oracle, full step scaled by the group counts from " + "; ".join(sample)
                        + f"; host has {len(os.sched_getaffinity(0))} usable cores")}
+
+
+def measured_peaks():
+    """The matrix-core and HBM rates the GPU sustains on their own
+    (libmoprobe.so, include/mo_probe.h), or None when the probe library is
+    missing or fails."""
+    import ctypes
+    path = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_amd", "libmoprobe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.mo_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    L.mo_probe_hbm.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                               ctypes.POINTER(ctypes.c_double)]
+    tf, rd, cp = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    if L.mo_probe_mfma_bf16(20000, 3, ctypes.byref(tf)) != 0:
+        return None
+    if L.mo_probe_hbm(4 << 30, 3, ctypes.byref(rd), ctypes.byref(cp)) != 0:
+        return None
+    return {"bf16_mfma_tflops": tf.value, "hbm_read_gbs": rd.value, "hbm_copy_gbs": cp.value,
+            "method": "register-only v_mfma_f32_32x32x16_bf16 loop, 2 waves per SIMD on every CU; "
+                      "4 GiB read-only and copy streams (copy counts read + write)"}
 
 
 FP64_PEAK_TFLOPS = 78.6       # fp64 vector and matrix
@@ -248,7 +299,7 @@ def main():
 
     step_no = [0]
 
-    hidden = float(max(max(g.rows, g.cols) for g in wl.mats))
+    hidden = float(wl.hidden)
 
     def opt_step():
         step_no[0] += 1
@@ -288,6 +339,7 @@ def main():
             kernels[c] = {"launches": n, "mean_ms": ms / n, "rate": rate, "unit": unit,
                           "frac": rate / (peak if unit == "TFLOP/s" else HBM_PEAK_GBS)}
     upd = prof["update"]
+    peaks = None if args.no_probe else measured_peaks()
     roofline = None
     if upd[0]:
         ach = upd[2] / (upd[1] * 1e-3) / 1e12
@@ -295,10 +347,17 @@ def main():
                     "frac": ach / peak, "traffic": measured_traffic(wl.key, _is_update_gemm),
                     "kernel": "ns_gemm update X <- aX + PX",
                     "flops_per_launch": upd[2] / upd[0], "mean_launch_ms": upd[1] / upd[0]}
+        if peaks and wl.ns_dtype == torch.bfloat16:
+            roofline["measured_peak"] = peaks["bf16_mfma_tflops"]
+            roofline["frac_of_measured_peak"] = ach / peaks["bf16_mfma_tflops"]
+    if peaks:
+        for k in kernels.values():
+            if k["unit"] == "GB/s":
+                k["frac_of_measured_copy"] = k["rate"] / peaks["hbm_copy_gbs"]
     ew_bytes = wl.n_elems * W.muon_elementwise_bytes_per_elem(wl) + \
         (wl.n_vec_elems * W.ADAMW_BYTES_PER_ELEM if wl.vecs else 0)
     line = {
-        "metric": "Muon optimizer steps/s (+ Newton-Schulz TFLOP/s, % of bf16 MFMA peak)",
+        "metric": "Muon optimizer steps/s + Newton-Schulz TFLOP/s (% bf16 MFMA peak) per config",
         "value": steps_per_s, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
@@ -318,6 +377,7 @@ def main():
         "elementwise_alg_gb_per_step": ew_bytes / 1e9,
         "kernels": kernels,
         "roofline": roofline,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, T, A)

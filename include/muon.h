@@ -23,10 +23,12 @@
  *   Memory   All tensor pointers are DEVICE pointers on the current HIP
  *            device, row-major and contiguous (leading dimension = cols),
  *            16-byte aligned.  The caller owns every buffer, including the
- *            workspace.  The library never allocates device memory inside a
- *            step; only mo_muon_plan_create allocates (its descriptor table).
- *            Descriptor arrays (mo_tensor) are HOST memory, read during the
- *            call only.
+ *            workspace.  The library never allocates device or pinned host
+ *            memory inside a step; only mo_muon_plan_create allocates (its
+ *            descriptor table).  Descriptor arrays (mo_tensor) are HOST
+ *            memory, read during the call only: one-shot calls copy them to
+ *            the workspace with small kernels that carry the table in their
+ *            launch arguments, so no call waits for an earlier one.
  *   Streams  `stream` is a hipStream_t passed as void* (NULL = the null
  *            stream).  Work is enqueued on it in order, and calls return
  *            without waiting for the GPU.  Calls on different streams with
@@ -39,7 +41,13 @@
  *            Faults during execution surface at the caller's next
  *            synchronisation as a HIP error (set MO_DEBUG_SYNC=1 in the
  *            environment to synchronise after every launch and map them to
- *            MO_EHIP).  NaN and Inf propagate per IEEE arithmetic.
+ *            MO_EHIP).  NaN and Inf propagate per IEEE arithmetic: a
+ *            NaN or Inf in a matrix's gradient or momentum reaches its
+ *            Frobenius norm, so that matrix's whole update -- and its
+ *            parameter -- becomes NaN, and its update_rms entry is NaN
+ *            (the per-matrix non-finite flag); the momentum is non-finite
+ *            only where its inputs were; every other matrix of the call is
+ *            unaffected.
  *   Threads  Entry points are thread-safe except that a plan must not be
  *            stepped from two threads at once.
  *   Tuning   Environment switches for tests and measurement only (MO_TILE
@@ -63,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MO_ABI_VERSION 3
+#define MO_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum mo_status {
@@ -193,6 +201,21 @@ typedef enum mo_scaling {
  * Returns MO_OK or MO_EINVAL (plan unchanged). */
 int mo_muon_plan_set_scaling(mo_muon_plan* plan, int scaling, float hidden);
 
+/* Rebinds the plan's gradients (section 2.1, Eq. 1's G_t) to new buffers
+ * without recreating it, for callers whose gradient tensors move between
+ * steps (a framework that frees gradients after each step).  grads[i] is the
+ * gradient of the plan's tensor i (the order given to mo_muon_plan_create),
+ * same shape and dtype as before, 16-byte aligned, not overlapping any
+ * param, momentum or other gradient of the plan.  When every pointer is
+ * unchanged nothing is enqueued; otherwise the descriptor table is updated
+ * on `stream` by one small kernel per 96 tensors (no host synchronisation),
+ * so later plan steps on the same stream use the new gradients.  Steps of
+ * the plan queued on other streams must be ordered by the caller.
+ * Validation is complete before anything changes: MO_EINVAL leaves the plan
+ * as it was.  Returns MO_OK, MO_EINVAL or MO_EHIP. */
+int mo_muon_plan_set_grads(mo_muon_plan* plan, const void* const* grads,
+                           int64_t count, void* stream);
+
 /* Frees the plan's descriptor table (synchronises the device first). */
 int mo_muon_plan_destroy(mo_muon_plan* plan);
 
@@ -269,7 +292,7 @@ typedef enum mo_kernel_class {
     MO_K_NORM = 1,         /* per-matrix norm finalisation                   */
     MO_K_GRAM = 2,         /* S = X X^T (lower tiles, mirrored)              */
     MO_K_POLY = 3,         /* P = b S + c S S (lower tiles, mirrored)        */
-    MO_K_UPDATE = 4,       /* X <- a X + P X, both layouts                   */
+    MO_K_UPDATE = 4,       /* X <- P' X = a X + P X (P' = a I + b S + c S S)  */
     MO_K_APPLY = 5,        /* last update fused with scale, decay and apply  */
     MO_K_APPLY_X0 = 6,     /* apply for ns_steps = 0                         */
     MO_K_RMS = 7,          /* update-RMS finalisation                        */

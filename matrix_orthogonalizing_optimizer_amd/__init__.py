@@ -169,7 +169,10 @@ class MuonPlan:
             raise ValueError("params, grads and moms must have the same length")
         self.n = n
         self.device = params[0].device if n else torch.device("cuda")
+        # the plan holds raw pointers: keep the tensors alive while it lives
         self._keep = (list(params), list(grads), list(moms))
+        self._grad_meta = [(tuple(g.shape), g.dtype) for g in grads]
+        self._grads_bound = True
         gdt = _dtype_code(_common_dtype(grads, "grads"), "grads") if n else MO_F32
         mdt = _dtype_code(_common_dtype(moms, "moms"), "moms") if n else MO_F32
         arr = _mk_tensors(params, grads, moms)
@@ -191,6 +194,8 @@ class MuonPlan:
         (0.2 sqrt(hidden), Eq. 5) or "update_norm" (0.2 / RMS(X_N), Eq. 6)."""
         if self._h is None:
             raise RuntimeError("plan was closed")
+        if not self._grads_bound:
+            raise RuntimeError("gradients were released: call set_grads() before step()")
         if scaling not in _SCALINGS:
             raise ValueError(f"scaling must be one of {sorted(_SCALINGS)}")
         if scaling == "hidden" and hidden is None:
@@ -203,6 +208,35 @@ class MuonPlan:
         check(lib().mo_muon_plan_step(self._h, lr, wd, mu, int(nesterov), ns_steps, _abc(abc),
                                       rms_scale, eps, _ptr(update_rms), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), sh))
+
+    def set_grads(self, grads: Sequence[torch.Tensor], stream=None) -> None:
+        """Rebind the plan's gradients (``mo_muon_plan_set_grads``): same
+        shapes and dtype, new buffers.  Nothing is enqueued when the pointers
+        are unchanged; otherwise one small kernel per 96 matrices updates the
+        descriptor table on the stream, with no host synchronisation."""
+        if self._h is None:
+            raise RuntimeError("plan was closed")
+        grads = list(grads)
+        if len(grads) != self.n:
+            raise ValueError(f"expected {self.n} gradients, got {len(grads)}")
+        for i, (g, (shape, dt)) in enumerate(zip(grads, self._grad_meta)):
+            if tuple(g.shape) != shape or g.dtype != dt:
+                raise ValueError(f"grad {i}: expected {shape} {dt}, got {tuple(g.shape)} {g.dtype}")
+        arr = (ctypes.c_void_p * max(self.n, 1))(*[_ptr(g) for g in grads])
+        with torch.cuda.device(self.device):
+            check(lib().mo_muon_plan_set_grads(self._h, arr, self.n,
+                                               _stream_handle(self.device, stream)))
+        self._keep = (self._keep[0], grads, self._keep[2])
+        self._grads_bound = True
+
+    def release_grads(self) -> None:
+        """Drop the plan's references to its gradients once a step using
+        them is queued (torch orders any reuse of their memory after the
+        work already queued on the stream), so a framework that makes fresh
+        gradients every step does not hold two sets.  The next step needs
+        ``set_grads`` first."""
+        self._keep = (self._keep[0], None, self._keep[2])
+        self._grads_bound = False
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
@@ -360,7 +394,7 @@ class MuonAdamW:
         self.exp_avg_sq = [torch.zeros_like(p, dtype=torch.float32) for p in self.adamw_params]
         self.t = 0
         self._plan: Optional[MuonPlan] = None
-        self._plan_key = None
+        self.plans_created = 0
 
     def _grads(self, ps):
         gs = [p.grad for p in ps]
@@ -368,19 +402,32 @@ class MuonAdamW:
             raise RuntimeError("every parameter needs a gradient before step()")
         return gs
 
+    def zero_grad(self, set_to_none: bool = True) -> None:
+        """As ``torch.optim.Optimizer.zero_grad``: drop (or zero) every
+        parameter's gradient."""
+        for p in self.muon_params + self.adamw_params:
+            if p.grad is None:
+                continue
+            if set_to_none:
+                p.grad = None
+            else:
+                p.grad.zero_()
+
     def step(self, lr: Optional[float] = None, update_rms: Optional[torch.Tensor] = None) -> None:
         lr = self.lr if lr is None else lr
         self.t += 1
         if self.muon_params:
             gs = self._grads(self.muon_params)
-            key = tuple(g.data_ptr() for g in gs)
-            if self._plan is None or key != self._plan_key:
-                if self._plan is not None:
-                    self._plan.close()
+            if self._plan is None:
+                # the plan binds params and momenta once; gradients that move
+                # between steps (zero_grad(set_to_none=True)) are rebound
                 self._plan = MuonPlan(self.muon_params, gs, self.momentum, self.ns_dtype)
-                self._plan_key = key
+                self.plans_created += 1
+            else:
+                self._plan.set_grads(gs)
             self._plan.step(lr=lr, wd=self.wd, mu=self.mu, nesterov=self.nesterov,
                             ns_steps=self.ns_steps, update_rms=update_rms)
+            self._plan.release_grads()
         if self.adamw_params:
             adamw_step(self.adamw_params, self._grads(self.adamw_params), self.exp_avg,
                        self.exp_avg_sq, lr=lr, step=self.t, wd=self.wd, beta1=self.betas[0],

@@ -63,6 +63,7 @@ _SIGS = {
                                      _c.POINTER(_c.c_float), _c.c_float, _c.c_float,
                                      _P, _P, _c.c_size_t, _P]),
     "mo_muon_plan_set_scaling": (_c.c_int, [_P, _c.c_int, _c.c_float]),
+    "mo_muon_plan_set_grads": (_c.c_int, [_P, _c.POINTER(_P), _c.c_int64, _P]),
     "mo_muon_plan_destroy": (_c.c_int, [_P]),
     "mo_adamw_step": (_c.c_int, [_c.POINTER(MoTensor), _c.c_int64, _c.c_int, _c.c_float,
                                  _c.c_float, _c.c_double, _c.c_double, _c.c_float, _c.c_int64, _P]),

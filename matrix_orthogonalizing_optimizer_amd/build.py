@@ -21,6 +21,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 SOURCES = ["ns_gemm.hip", "ns_small.hip", "elementwise.hip", "svd_entropy.hip", "muon_api.hip",
            "svd_api.hip"]
+# roofline probes of the benchmark: a library of their own, not the optimizer's ABI
+PROBE_LIB = os.path.join(PKG, "libmoprobe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -42,27 +45,39 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link ``libmuon.so``; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
-        for out in ex.map(_run, cmds):
-            if verbose and out.strip():
-                print(out)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     # every symbol must resolve (a kernel whose host-side stub was not
     # emitted would otherwise only fail when the library is first loaded)
     _run(["python3", "-c", f"import ctypes; ctypes.CDLL({tmp!r}, mode=ctypes.RTLD_LOCAL)"])
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources, link ``libmuon.so`` and the probe library;
+    returns the path of ``libmuon.so``."""
+    os.makedirs(BUILD, exist_ok=True)
+    cmds = []
+
+    def objs_of(srcs):
+        out = []
+        for src in srcs:
+            obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+            out.append(obj)
+            cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        return out
+
+    objs = objs_of(SOURCES)
+    probe_objs = objs_of(PROBE_SOURCES)
+    with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+        for out in ex.map(_run, cmds):
+            if verbose and out.strip():
+                print(out)
+    _link(objs, LIB)
+    _link(probe_objs, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -3,8 +3,9 @@
 //  * prep:  momentum M <- mu M + G (section 2.1, Eq. 1), the Nesterov input
 //           N = mu M + G (paragraph after Eq. 1), per-tile fp32 partial sums
 //           of N^2 for the Frobenius norm (text before Eq. 2), and N written
-//           in the Newton-Schulz dtype in both layouts (row-major iterate X
-//           and its transpose) -- one pass over G and M.
+//           once, in the Newton-Schulz dtype, as the oriented blocked iterate
+//           X_0 (transposed through LDS for tall parameters) -- one pass over
+//           G and M.
 //  * norm:  per-matrix fp64 combine of the partials -> r = 1/(||N||_F + eps).
 //           X_0 = r N is never materialised: r is applied in the epilogues of
 //           the first Gram and Update products.
@@ -404,6 +405,28 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs p) {
     store4<true>(T.m, F32, off, nv[h], vec, m[h]);
     store4<true>(T.v, F32, off, nv[h], vec, v[h]);
   }
+}
+
+// Descriptor upload carried in the kernel arguments: the runtime copies the
+// arguments when the launch is enqueued, so the host neither stages the
+// table in pinned memory nor waits for an earlier upload to finish, and the
+// launch can be captured into a graph like any other.
+__global__ __launch_bounds__(kDescPerCopy) void desc_copy_kernel(DescCopyArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.count) a.dst[i] = a.d[i];
+}
+
+hipError_t launch_desc_copy(const MatDesc* src, int64_t count, MatDesc* dst, hipStream_t s) {
+  for (int64_t i0 = 0; i0 < count; i0 += kDescPerCopy) {
+    DescCopyArgs a;
+    a.count = static_cast<int>(count - i0 < kDescPerCopy ? count - i0 : kDescPerCopy);
+    a.dst = dst + i0;
+    for (int k = 0; k < a.count; ++k) a.d[k] = src[i0 + k];
+    hipLaunchKernelGGL(desc_copy_kernel, dim3(1), dim3(kDescPerCopy), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_prep(const PrepArgs& a, int chunk, hipStream_t s) {

@@ -23,7 +23,8 @@ static_assert(sizeof(MatDesc) == 32, "descriptor layout");
 
 // Momentum / X_0 preparation over one shape group (a "bin") chunk.
 // Tiles of 64x64 cover the padded natural domain [A_pad, B_pad] of every
-// matrix; each tile writes the Newton-Schulz input in both layouts.
+// matrix; each tile writes its part of the Newton-Schulz input X_0 in the
+// oriented, blocked layout (one layout: the update reads X K-major from it).
 struct PrepArgs {
   const MatDesc* desc;   // chunk's descriptors (chunk-local index)
   void* x;               // [chunk] blocked [m_pad, n_pad]  (ns dtype), oriented
@@ -162,6 +163,15 @@ struct AdamArgs {
 };
 constexpr int kAdamElemsPerBlock = 2048;   // 256 threads x 8
 
+// Descriptor upload by kernel arguments: up to kDescPerCopy descriptors
+// (3 KiB) per launch of a one-workgroup copy kernel.
+constexpr int kDescPerCopy = 96;
+struct DescCopyArgs {
+  MatDesc d[kDescPerCopy];
+  MatDesc* dst;
+  int count;
+};
+
 // Tile configurations of the GEMM (square tiles).
 enum TileCfg : int { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
 int tile_size(TileCfg t);
@@ -176,5 +186,7 @@ hipError_t launch_apply_x0(const ApplyX0Args& a, int chunk, hipStream_t s);
 hipError_t launch_small(const SmallArgs& a, int total, hipStream_t s);
 hipError_t launch_rms(const RmsArgs& a, int chunk, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t blocks, hipStream_t s);
+// copies count host descriptors to dst (device) on s, 96 per launch
+hipError_t launch_desc_copy(const MatDesc* src, int64_t count, MatDesc* dst, hipStream_t s);
 
 }  // namespace mo

@@ -4,7 +4,7 @@
 // oriented shape, tile choice, workspace layout, the descriptor table, and
 // the launch sequence of one step:
 //   per shape group ("bin"), per chunk of matrices that fits the workspace:
-//     prep (momentum, Nesterov input, norm partials, X_0 in both layouts)
+//     prep (momentum, Nesterov input, norm partials, X_0 in the oriented layout)
 //     norm (r = 1 / (||N||_F + eps))
 //     N x { Gram, Poly, Update }   -- the last Update applies the step
 //     rms (optional update RMS)
@@ -687,42 +687,14 @@ int run_step(const HostPlan& plan, const MatDesc* d_desc, const Hyper& h, float*
   return MO_OK;
 }
 
-// Pinned host staging for one-shot descriptor uploads: reused once the
-// previous upload from it has completed.
-struct Staging {
-  void* host = nullptr;
-  size_t bytes = 0;
-  hipEvent_t done = nullptr;
-  bool pending = false;
-};
-thread_local Staging g_stage;
-
+// One-shot calls copy the descriptor table into the workspace with small
+// kernels that carry it in their arguments (launch_desc_copy): the host
+// neither stages it in pinned memory nor waits on an earlier call's upload.
 int upload_descs(const HostPlan& plan, void* dst, hipStream_t s) {
-  const size_t bytes = plan.descs.size() * sizeof(MatDesc);
-  if (bytes == 0) return MO_OK;
-  hipError_t e;
-  if (g_stage.pending) {
-    if ((e = hipEventSynchronize(g_stage.done)) != hipSuccess)
-      return fail(MO_EHIP, "staging wait failed: %s", hipGetErrorString(e));
-    g_stage.pending = false;
-  }
-  if (g_stage.bytes < bytes) {
-    if (g_stage.host) (void)hipHostFree(g_stage.host);
-    g_stage.host = nullptr;
-    g_stage.bytes = 0;
-    if ((e = hipHostMalloc(&g_stage.host, bytes, 0)) != hipSuccess)
-      return fail(MO_EHIP, "pinned staging allocation failed: %s", hipGetErrorString(e));
-    g_stage.bytes = bytes;
-  }
-  if (!g_stage.done && (e = hipEventCreateWithFlags(&g_stage.done, hipEventDisableTiming)) != hipSuccess)
-    return fail(MO_EHIP, "event creation failed: %s", hipGetErrorString(e));
-  std::memcpy(g_stage.host, plan.descs.data(), bytes);
-  if ((e = hipMemcpyAsync(dst, g_stage.host, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
-    return fail(MO_EHIP, "descriptor upload failed: %s", hipGetErrorString(e));
-  if ((e = hipEventRecord(g_stage.done, s)) != hipSuccess)
-    return fail(MO_EHIP, "event record failed: %s", hipGetErrorString(e));
-  g_stage.pending = true;
-  return MO_OK;
+  if (plan.descs.empty()) return MO_OK;
+  return checked(launch_desc_copy(plan.descs.data(), static_cast<int64_t>(plan.descs.size()),
+                                  static_cast<MatDesc*>(dst), s),
+                 s, "descriptor upload");
 }
 
 Hyper make_hyper(float lr, float wd, float mu, int nesterov, int ns_steps, const float* abc, float rms_scale,
@@ -853,6 +825,45 @@ int mo_muon_plan_set_scaling(mo_muon_plan* plan, int scaling, float hidden) {
   plan->scaling = scaling;
   plan->hidden = scaling == MO_SCALE_HIDDEN ? hidden : 0.0f;
   return MO_OK;
+}
+
+int mo_muon_plan_set_grads(mo_muon_plan* plan, const void* const* grads, int64_t count, void* stream) {
+  if (!plan) return fail(MO_EINVAL, "plan is NULL");
+  HostPlan& hp = plan->plan;
+  if (count != hp.count) return fail(MO_EINVAL, "count %lld does not match the plan's %lld tensors",
+                                      static_cast<long long>(count), static_cast<long long>(hp.count));
+  if (count > 0 && !grads) return fail(MO_EINVAL, "grads is NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(MO_EINVAL, "plan was created on device %d, current device is %d", plan->device, dev);
+  // validate in full against the plan's other buffers before changing anything
+  std::vector<Range> ranges;
+  std::vector<const void*> by_desc(hp.descs.size());
+  bool same = true;
+  for (const Bin& b : hp.bins) {
+    const uintptr_t ne = static_cast<uintptr_t>(b.m) * static_cast<uintptr_t>(b.n);
+    for (int k = b.first; k < b.first + b.count; ++k) {
+      const MatDesc& d = hp.descs[k];
+      const void* g = grads[d.out_index];
+      if (!g) return fail(MO_EINVAL, "grad %d is NULL", d.out_index);
+      if (!aligned16(g)) return fail(MO_EINVAL, "grad %d must be 16-byte aligned", d.out_index);
+      by_desc[k] = g;
+      same = same && g == d.grad;
+      ranges.push_back({reinterpret_cast<uintptr_t>(d.param), reinterpret_cast<uintptr_t>(d.param) + ne * 4,
+                        d.out_index, "param"});
+      ranges.push_back({reinterpret_cast<uintptr_t>(g), reinterpret_cast<uintptr_t>(g) + ne * dt_size(hp.grad_dt),
+                        d.out_index, "grad"});
+      ranges.push_back({reinterpret_cast<uintptr_t>(d.mom),
+                        reinterpret_cast<uintptr_t>(d.mom) + ne * dt_size(hp.mom_dt), d.out_index, "momentum"});
+    }
+  }
+  if (same) return MO_OK;
+  int rc;
+  if ((rc = check_overlap(ranges))) return rc;
+  for (size_t k = 0; k < hp.descs.size(); ++k) hp.descs[k].grad = by_desc[k];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return checked(launch_desc_copy(hp.descs.data(), static_cast<int64_t>(hp.descs.size()), plan->d_desc, s), s,
+                 "descriptor upload");
 }
 
 int mo_muon_plan_destroy(mo_muon_plan* plan) {

@@ -97,7 +97,7 @@ def _map_over_x(y_over, x, steps, abc):
 
 
 def ns_closed_form_gram(N, steps: int = NS_STEPS, abc=NS_COEFFS,
-                        eps: float = NORM_EPS):
+                        eps: float = NORM_EPS, eig=None):
     """The closed form of ``ns_closed_form`` taken through ``short_side_eig``.
 
     ``U f^N(S / nu) V^T = U diag(f^N(sigma_i / nu) / sigma_i) U^T N`` (wide;
@@ -114,8 +114,23 @@ def ns_closed_form_gram(N, steps: int = NS_STEPS, abc=NS_COEFFS,
     return N @ K if tall else K @ N
 
 
+def per_sigma_projections_gram(X, N, eig=None):
+    """``(sigma, u_i^T X v_i)`` for every singular triplet of ``N`` with
+    ``sigma_i > 0`` (see ``per_sigma_deviation_gram``), largest first."""
+    N = np.asarray(N, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    if N.shape != X.shape:
+        raise ValueError("X and N must have the same shape")
+    sigma, Q, tall = short_side_eig(N) if eig is None else eig
+    keep = sigma > 0.0
+    B = X.T @ N if tall else X @ N.T               # short x short
+    Qk = Q[:, keep]
+    return sigma[keep], np.einsum("ij,ij->j", Qk, B @ Qk) / sigma[keep]
+
+
 def per_sigma_deviation_gram(X, N, steps: int = NS_STEPS, abc=NS_COEFFS,
-                             eps: float = NORM_EPS, rel_floor: float = 0.0) -> float:
+                             eps: float = NORM_EPS, rel_floor: float = 0.0,
+                             eig=None) -> float:
     """``per_sigma_deviation`` with the singular triplets of ``N`` from
     ``short_side_eig``.
 
@@ -125,22 +140,17 @@ def per_sigma_deviation_gram(X, N, steps: int = NS_STEPS, abc=NS_COEFFS,
     ``N`` is needed.  Directions with ``sigma_i <= rel_floor * sigma_1`` (and
     exact zeros, whose partner is undefined) are left out; the Gram matrix
     returns exact zeros of N as singular values near ``1e-8 sigma_1``, so a
-    rank-deficient input needs a floor above that.
+    rank-deficient input needs a floor above that.  ``eig``:
+    ``short_side_eig(N)`` if already computed.
     """
     N = np.asarray(N, dtype=np.float64)
-    X = np.asarray(X, dtype=np.float64)
-    if N.shape != X.shape:
-        raise ValueError("X and N must have the same shape")
-    sigma, Q, tall = short_side_eig(N)
+    sig, proj = per_sigma_projections_gram(X, N, eig)
     nu = float(np.sqrt(np.sum(N * N)))
-    target = scalar_map(sigma / (nu + eps), steps, abc)
-    B = X.T @ N if tall else X @ N.T               # short x short
-    keep = sigma > max(rel_floor * (sigma[0] if sigma.size else 0.0), 0.0)
+    keep = sig > rel_floor * (sig[0] if sig.size else 0.0)
     if not np.any(keep):
         return 0.0
-    Qk = Q[:, keep]
-    proj = np.einsum("ij,ij->j", Qk, B @ Qk) / sigma[keep]
-    return float(np.max(np.abs(proj - target[keep])))
+    target = scalar_map(sig[keep] / (nu + eps), steps, abc)
+    return float(np.max(np.abs(proj[keep] - target)))
 
 
 def rel_fro(x, ref) -> float:

@@ -88,3 +88,38 @@ def test_committed_profiles_name_existing_sources():
             for s in rec["sources"]:
                 assert os.path.exists(os.path.join(ROOT, s)), (f, s)
             assert rec["kernels"], f
+
+
+def test_cpu_baseline_covers_every_group_and_extrapolates():
+    """Every shape group is timed (none dropped on a budget); a group above
+    the direct-timing threshold is timed at N = 0 and N = 1 and extrapolated,
+    and says so; the CPU model is recorded."""
+    import bench
+
+    wl = W.Workload(key="t", description="t", cid=98,
+                    mats=(W.MatGroup("a", 64, 96, 3), W.MatGroup("b", 160, 96, 2)),
+                    vecs=(W.VecGroup("v", (40,), 2),), ns_steps=5,
+                    grad_dtype=W.WORKLOADS["dense800m"].grad_dtype,
+                    mom_dtype=W.WORKLOADS["dense800m"].mom_dtype,
+                    ns_dtype=W.WORKLOADS["dense800m"].ns_dtype)
+    T = W.make_muon_tensors(wl, "cpu")
+    A = W.make_adamw_tensors(wl, "cpu")
+    a_flops = W.ns_flops(64, 96, 5)[1]
+    out = bench.cpu_baseline(wl, T, A, direct_flops=a_flops)     # group b above it
+    assert out["kind"] == "oracle" and out["value"] > 0 and out["cores"] >= 1
+    assert out["cpu"]
+    s = out["sample"]
+    assert "1 of 3 [64,96] (" in s
+    assert "1 of 2 [160,96] at N=0" in s and "extrapolated to N=5" in s
+    assert "1 of 2 AdamW [40]" in s
+
+
+def test_eq5_hidden_size_is_the_model_width():
+    """Section 3.1, Eq. 5 scales by 0.2 sqrt(H) with H the model's hidden
+    size -- not the largest matrix side (6144 for the 800M MLP)."""
+    assert W.WORKLOADS["dense800m"].hidden == 1536
+    assert W.WORKLOADS["llama1p5b_gqa"].hidden == 2048
+    assert W.WORKLOADS["moe_share"].hidden == 2048
+    assert W.WORKLOADS["large_n5"].hidden == 8192
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert "hidden = float(wl.hidden)" in src

@@ -45,10 +45,23 @@ def _check_common(d, steps, warmup):
 def test_bench_default_line():
     d = _run(["--steps", "2", "--warmup", "1"])
     _check_common(d, 2, 1)
-    assert d["config"]["workload"] == "dense800m" and d["unit"] == "steps/s"
+    assert d["config"]["workload"] == "large_n5" and d["unit"] == "steps/s"
     assert d["roofline"]["bound"] == "mfma" and d["roofline"]["unit"] == "TFLOP/s"
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["cpu"]
+    for shape in ("[8192,8192]", "[8192,28672]", "[28672,8192]"):
+        assert shape in cpu["sample"], shape
+    pk = d["measured_peaks"]
+    assert 500 < pk["bf16_mfma_tflops"] < 2600 and 1000 < pk["hbm_read_gbs"] < 9000
+    assert 0 < d["roofline"]["frac_of_measured_peak"] < 1.2
+
+
+def test_bench_800m_line():
+    d = _run(["--workload", "dense800m", "--steps", "2", "--warmup", "1", "--no-probe"])
+    _check_common(d, 2, 1)
+    assert d["config"]["workload"] == "dense800m" and "adamw" in d["kernels"]
+    assert "[32000, 1536]" in d["cpu_baseline"]["sample"]
 
 
 def test_bench_svd_entropy_line():

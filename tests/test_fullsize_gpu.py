@@ -3,23 +3,23 @@ benchmark times (one plan over every matrix of the workload, full
 workspace).
 
 * 800M dense, 1.5B GQA, the MoE share and the per-head split of the GQA
-  attention (960 matrices [128, 2048]): sampled matrices (every shape
-  group, both orientations; for the MoE share all 32 non-expert matrices
-  and 16 experts) are checked one by one against the fp64 oracle, started
-  from the same pre-step state: update relative Frobenius error <= 2e-2,
-  per-singular-value deviation <= 0.05 (one matrix per shape group), bf16
-  momentum within half an ulp.  AdamW tensors of the 800M step likewise.
-  (MoE share: 16 of the 32 non-expert matrices and 18 experts.)
-* Large 8192-class matrices (N = 5 and N = 10): one fp64 oracle step costs
-  ~1e13-4e13 flops per matrix, too slow here, so the check is (a) the
-  momentum at sampled elements against the oracle's elementwise formula and
-  (b) properties every Newton-Schulz output has at any size: N X_N^T is
-  symmetric (X_N = U f(S) V^T for N = U S V^T; with bf16 iterates the
-  relative asymmetry is of the order of their ~1e-2 relative error, a
-  mis-placed tile or transpose gives O(1)), the spectral norm of X_N
-  stays inside the band of the scalar map (<= 1.21 for N = 5, <= 1.21 for
-  N = 10 too: its iterates stay below the largest value 1.2 the map
-  reaches), and the update RMS lies in the band 0.2 * [0, 1.21].
+  attention (960 matrices [128, 2048]): sampled matrices are checked one by
+  one against the fp64 oracle, started from the same pre-step state: update
+  relative Frobenius error <= 2e-2, per-singular-value deviation <= 0.05
+  (one matrix per shape group), bf16 momentum within half an ulp.  The
+  samples are the first and last matrix of every shape group (both
+  orientations); for the MoE share, every other one of its 32 non-expert
+  matrices (16) and 6 experts from each of the 3 expert groups (18).
+  AdamW tensors of the 800M step likewise.
+* The large 8192-class workloads have their own oracle-parity test
+  (``test_large_parity_gpu.py``).
+* One matrix of 2^30 elements in both orientations: the momentum at sampled
+  elements against the oracle's elementwise formula, and properties every
+  Newton-Schulz output has at any size: N X_N^T is symmetric (X_N = U f(S)
+  V^T for N = U S V^T; with bf16 iterates the relative asymmetry is of the
+  order of their ~1e-2 relative error, a mis-placed tile or transpose gives
+  O(1)), the spectral norm of X_N stays inside the band of the scalar map
+  (<= 1.21 for N = 5), and the update RMS lies in the band 0.2 * [0, 1.21].
 """
 
 from __future__ import annotations
@@ -119,47 +119,6 @@ def test_full_dense800m_adamw(mod):
         p1 = f64(A.params[k])
         tol = 1e-5 * np.abs(p0 - Wo) + np.abs(Wo) * 2.0 ** -23 + 1e-30
         assert np.all(np.abs(p1 - Wo) <= tol)
-
-
-@pytest.mark.parametrize("key", ["large_n5", "large_n10"])
-def test_full_large_properties(mod, key):
-    wl = W.WORKLOADS[key]
-    T = W.make_muon_tensors(wl, "cuda")
-    groups = [0, 16, 32]                 # first [8192,8192], [8192,28672], [28672,8192]
-    gen = torch.Generator().manual_seed(7)
-    snap = {}
-    for i in groups:
-        numel = T.params[i].numel()
-        idx = torch.randint(0, numel, (4096,), generator=gen)
-        snap[i] = (idx, f64(T.params[i].flatten()[idx.cuda()]), f64(T.grads[i].flatten()[idx.cuda()]),
-                   f64(T.moms[i].flatten()[idx.cuda()]), T.params[i].clone(), T.grads[i].float().clone())
-    rms = _run_step(mod, wl, T, wl.ns_steps)
-    for i in groups:
-        idx, p0, g0, m0, P0, N = snap[i]
-        M1 = f64(T.moms[i].flatten()[idx.cuda()])
-        Mo, _ = mo.momentum_update(m0, g0, 0.95, True)
-        tol = np.abs(Mo) * (2.0 ** -8 + 2.0 ** -20) + (np.abs(0.95 * m0) + np.abs(g0)) * 2.0 ** -22 + 1e-30
-        assert np.all(np.abs(M1 - Mo) <= tol), (key, i)
-        r, c = T.params[i].shape
-        step = HYP["lr"] * 0.2 * math.sqrt(max(r, c))
-        X = ((P0 - T.params[i]) - HYP["lr"] * HYP["wd"] * P0) / step      # recovered X_N (fp32)
-        N = N * 1.95                                                        # Nesterov input at step 1
-        # N X^T symmetric (on the short side)
-        A = (N @ X.T) if r <= c else (N.T @ X)
-        asym = (torch.linalg.norm(A - A.T) / torch.linalg.norm(A)).item()
-        assert asym <= 5e-2, (key, i, asym)
-        # spectral norm of X inside the map's band (power iteration)
-        v = torch.randn(X.shape[1], device="cuda")
-        for _ in range(30):
-            v = X.T @ (X @ v)
-            v = v / torch.linalg.norm(v)
-        smax = torch.linalg.norm(X @ v).item()
-        assert smax <= 1.25, (key, i, smax)
-        rms_scaled = 0.2 * math.sqrt(max(r, c)) * rms[i].item()
-        assert 0.05 <= rms_scaled <= 0.2 * 1.21, (key, i, rms_scaled)
-        print(f"{key} matrix {i} [{r},{c}]: asym {asym:.2e}, |X|_2 {smax:.3f}, scaled rms {rms_scaled:.3f}")
-        del A, X, P0, N
-    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("shape", [(8192, 131072), (131072, 8192)])

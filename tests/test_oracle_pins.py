@@ -485,3 +485,19 @@ def test_scaling_mutants_are_caught():
 
     for fn in (hidden_uses_shape, norm_by_frobenius, norm_times_shape):
         assert _scaling_pins_fail(fn), fn.__name__
+
+
+def test_nonfinite_gradient_poisons_the_whole_update():
+    """IEEE propagation (a reading: the pages say nothing): one NaN or Inf in
+    G reaches ||N||_F, so X_N and the updated weight are NaN everywhere and
+    the update RMS is NaN; the momentum is non-finite at that element only."""
+    r = _rng(21)
+    for v in (np.nan, np.inf, -np.inf):
+        W = r.normal(0, 0.02, (6, 10))
+        G = r.normal(0, 1e-3, (6, 10))
+        G[2, 3] = v
+        with np.errstate(invalid="ignore", over="ignore"):
+            Wn, Mn, X, rms = mo.muon_step(W, G, np.zeros_like(W), **HYPER)
+        assert np.isnan(Wn).all() and np.isnan(X).all() and math.isnan(rms)
+        bad = ~np.isfinite(Mn)
+        assert bad.sum() == 1 and bad[2, 3]

@@ -387,12 +387,7 @@ def test_plan_scaling_validation(mod):
 def test_step_variants(mod, variant):
     shapes = [(200, 456), (456, 200), (64, 64)]
     if variant.get("ns_steps") == 10:
-        # At N = 10 the near-zero singular values of a square matrix are
-        # lifted by about a^10 into the steepest part of the 10-fold map, so
-        # bf16 iterates cannot track them (a CPU model of the rounding shows
-        # per-sigma deviations of 0.06-0.4 there under either rounding
-        # placement); the N = 10 gate uses non-square shapes.
-        shapes = [(200, 456), (456, 200), (96, 300)]
+        shapes = [(200, 456), (456, 200), (96, 300), (64, 64)]
     Ps, Gs, Ms = _mixed_state(200, shapes)
     P0, G0, M0 = [f64(p) for p in Ps], [f64(g) for g in Gs], [f64(m) for m in Ms]
     hyp = dict(HYP, **variant)
@@ -408,9 +403,19 @@ def test_step_variants(mod, variant):
             X_rec = (P0[i] - f64(Ps[i]) - hyp["lr"] * hyp["wd"] * P0[i]) / (
                 hyp["lr"] * hyp["rms_scale"] * math.sqrt(max(r, c)))
             _, N = mo.momentum_update(M0[i], G0[i], hyp["mu"], hyp["nesterov"])
-            assert sp.per_sigma_deviation(X_rec, N, 10, eps=hyp["eps"]) <= 0.05
-            # reported bound: bf16 at N = 10 is not held to 2e-2
-            assert sp.rel_fro(P0[i] - f64(Ps[i]), P0[i] - Wo) <= 4e-2
+            dev = sp.per_sigma_deviation(X_rec, N, 10, eps=hyp["eps"])
+            fro = sp.rel_fro(P0[i] - f64(Ps[i]), P0[i] - Wo)
+            print(f"N = 10 {shapes[i]}: per-sigma {dev:.3e}, update rel_fro {fro:.3e}")
+            if r != c:
+                assert dev <= 0.05
+                # reported bound: bf16 at N = 10 is not held to 2e-2
+                assert fro <= 4e-2
+            else:
+                # square: near-zero singular values are lifted by ~a^10 into
+                # the steepest part of the 10-fold map, where bf16 iterates
+                # cannot follow them
+                assert dev <= 1.25
+                assert fro <= 0.1
         else:
             _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), hyp)
 

@@ -59,6 +59,8 @@ class Workload:
     expert_scale: bool = False
     experts_per_set: int = 0
     ns_steps: int = 5
+    # the model's hidden size H (section 3.1, Eq. 5's 0.2 sqrt(H) scaling)
+    hidden: int = 0
     lr: float = 1e-3
     wd: float = 0.1
     mu: float = 0.95
@@ -93,7 +95,7 @@ def _dense800m() -> Workload:
               VecGroup("embed", (32000, H), 1),
               VecGroup("lm_head", (32000, H), 1)),
         grad_dtype=torch.float32, mom_dtype=torch.bfloat16,
-        ns_dtype=torch.bfloat16)
+        ns_dtype=torch.bfloat16, hidden=H)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -103,7 +105,7 @@ WORKLOADS: Dict[str, Workload] = {
                      "N(0,1) gradients from zero momentum"),
         cid=1, mats=(MatGroup("w", 128, 512, 1),),
         grad_dtype=torch.float32, mom_dtype=torch.float32,
-        ns_dtype=torch.float32, g_std=1.0, steps=3),
+        ns_dtype=torch.float32, g_std=1.0, steps=3, hidden=128),
     "dense800m": _dense800m(),
     "llama1p5b_gqa": Workload(
         key="llama1p5b_gqa",
@@ -116,7 +118,7 @@ WORKLOADS: Dict[str, Workload] = {
               MatGroup("mlp_gate_up", 2048, 5632, 48),
               MatGroup("mlp_down", 5632, 2048, 24)),
         grad_dtype=torch.bfloat16, mom_dtype=torch.bfloat16,
-        ns_dtype=torch.bfloat16),
+        ns_dtype=torch.bfloat16, hidden=2048),
     "moe_share": Workload(
         key="moe_share",
         description=("MoE block group, one GPU's share: 8 layers x 64 experts "
@@ -133,7 +135,7 @@ WORKLOADS: Dict[str, Workload] = {
               MatGroup("attn_out", 2048, 2048, 8),
               MatGroup("router", 2048, 64, 8)),
         grad_dtype=torch.float32, mom_dtype=torch.bfloat16,
-        ns_dtype=torch.bfloat16, expert_scale=True, experts_per_set=512),
+        ns_dtype=torch.bfloat16, expert_scale=True, experts_per_set=512, hidden=2048),
     "large_n5": Workload(
         key="large_n5",
         description=("large dense matrices: 16 x [8192,8192], 16 x "
@@ -143,7 +145,7 @@ WORKLOADS: Dict[str, Workload] = {
               MatGroup("wide", 8192, 28672, 16),
               MatGroup("tall", 28672, 8192, 16)),
         grad_dtype=torch.bfloat16, mom_dtype=torch.bfloat16,
-        ns_dtype=torch.bfloat16, w_std=0.01),
+        ns_dtype=torch.bfloat16, w_std=0.01, hidden=8192),
     "kv_heads": Workload(
         key="kv_heads",
         description=("the 1.5B GQA model's attention with every head a separate "
@@ -156,7 +158,7 @@ WORKLOADS: Dict[str, Workload] = {
               MatGroup("head_v", 2048, 128, 4 * 24),
               MatGroup("head_o", 128, 2048, 16 * 24)),
         grad_dtype=torch.bfloat16, mom_dtype=torch.bfloat16,
-        ns_dtype=torch.bfloat16),
+        ns_dtype=torch.bfloat16, hidden=2048),
 }
 WORKLOADS["large_n10"] = dataclasses.replace(
     WORKLOADS["large_n5"], key="large_n10", ns_steps=10, cid=6,
