@@ -396,8 +396,8 @@ def test_step_variants(mod, variant):
     torch.cuda.synchronize()
     for i in range(len(Ps)):
         if hyp["ns_steps"] == 10:
-            # bf16 iterates at N=10 exceed 2e-2 Frobenius (the slope of the
-            # 10-fold map reaches ~86); gate on the per-sigma criterion only
+            # bf16 iterates at N=10 can exceed 2e-2 Frobenius (the slope of
+            # the 10-fold map reaches ~86); gate on the per-sigma criterion
             Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=mo.NS_COEFFS, **hyp)
             r, c = shapes[i]
             X_rec = (P0[i] - f64(Ps[i]) - hyp["lr"] * hyp["wd"] * P0[i]) / (
@@ -406,16 +406,11 @@ def test_step_variants(mod, variant):
             dev = sp.per_sigma_deviation(X_rec, N, 10, eps=hyp["eps"])
             fro = sp.rel_fro(P0[i] - f64(Ps[i]), P0[i] - Wo)
             print(f"N = 10 {shapes[i]}: per-sigma {dev:.3e}, update rel_fro {fro:.3e}")
-            if r != c:
-                assert dev <= 0.05
-                # reported bound: bf16 at N = 10 is not held to 2e-2
-                assert fro <= 4e-2
-            else:
-                # square: near-zero singular values are lifted by ~a^10 into
-                # the steepest part of the 10-fold map, where bf16 iterates
-                # cannot follow them
-                assert dev <= 1.25
-                assert fro <= 0.1
+            # measured on the GPU: per-sigma 0.012-0.039 (square 0.012),
+            # rel_fro 1.7-1.8e-2; bf16 at N = 10 is held to the per-sigma
+            # gate, and its Frobenius error is reported with a 4e-2 bound
+            assert dev <= 0.05
+            assert fro <= 4e-2
         else:
             _check_step(P0[i], G0[i], M0[i], f64(Ps[i]), f64(Ms[i]), rms[i].item(), hyp)
 
@@ -574,3 +569,4 @@ def test_steps_on_two_streams_use_separate_workspaces(mod):
         torch.cuda.synchronize()
         for got, want in zip(Pa + Ma + Pb + Mb, ref[0][0] + ref[0][1] + ref[1][0] + ref[1][1]):
             assert torch.equal(got, want)
+
