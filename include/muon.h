@@ -151,6 +151,31 @@ int mo_muon_step(const mo_tensor* tensors, int64_t count,
                  float* update_rms, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step of
+ * mo_muon_step, same arguments and results, with the library's own scratch
+ * memory in place of the caller's workspace.  The call allocates nothing
+ * (no hipMalloc, hipFree, pinned or library allocation).
+ *   Scratch: one static device array of MO_NOALLOC_SCRATCH_MIB MiB per GPU
+ *       the library runs on, held until the process ends; its address is
+ *       looked up on the first call on each device.  Matrices whose
+ *       minimum workspace (min_bytes of mo_muon_workspace_size) exceeds it
+ *       are rejected with MO_EWORKSPACE before anything is enqueued; below
+ *       the full size, shape groups are processed in chunks that fit, with
+ *       results identical to mo_muon_step's.
+ *   Sharing: every call on one GPU uses that GPU's scratch, so calls that
+ *       overlap on one GPU (different streams, or threads without ordering)
+ *       race; calls on one stream are ordered and safe.  Nothing in the
+ *       scratch needs clearing between calls (each kernel writes what it
+ *       later reads).
+ * Returns MO_OK, MO_EINVAL, MO_EWORKSPACE, MO_EUNSUPPORTED or MO_EHIP. */
+#define MO_NOALLOC_SCRATCH_MIB 256
+int mo_muon_step_noalloc(const mo_tensor* tensors, int64_t count,
+                         int grad_dtype, int mom_dtype, int ns_dtype,
+                         float lr, float wd, float mu, int nesterov,
+                         int ns_steps, const float* abc, float rms_scale,
+                         float eps, float* update_rms, void* stream);
+
 /* A plan binds one list of tensors (pointers, shapes, dtypes) so that
  * repeated steps skip validation, grouping and the descriptor upload of
  * mo_muon_step.  mo_muon_plan_create validates like mo_muon_step, allocates

@@ -55,6 +55,9 @@ _SIGS = {
                                 _c.c_float, _c.c_float, _c.c_float, _c.c_int, _c.c_int,
                                 _c.POINTER(_c.c_float), _c.c_float, _c.c_float,
                                 _P, _P, _c.c_size_t, _P]),
+    "mo_muon_step_noalloc": (_c.c_int, [_c.POINTER(MoTensor), _c.c_int64, _c.c_int, _c.c_int, _c.c_int,
+                                        _c.c_float, _c.c_float, _c.c_float, _c.c_int, _c.c_int,
+                                        _c.POINTER(_c.c_float), _c.c_float, _c.c_float, _P, _P]),
     "mo_muon_plan_create": (_c.c_int, [_c.POINTER(MoTensor), _c.c_int64, _c.c_int, _c.c_int,
                                        _c.c_int, _c.POINTER(_P)]),
     "mo_muon_plan_workspace_size": (_c.c_int, [_P, _c.POINTER(_c.c_size_t),

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 SOURCES = ["ns_gemm.hip", "ns_small.hip", "elementwise.hip", "svd_entropy.hip", "muon_api.hip",
-           "svd_api.hip"]
+           "svd_api.hip", "muon_noalloc.hip"]
 # roofline probes of the benchmark: a library of their own, not the optimizer's ABI
 PROBE_LIB = os.path.join(PKG, "libmoprobe.so")
 PROBE_SOURCES = ["peak_probe.hip"]

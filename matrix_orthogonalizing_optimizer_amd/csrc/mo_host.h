@@ -6,7 +6,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cstdint>
 #include <string>
+
+#include "muon.h"
 
 namespace mo {
 
@@ -37,5 +40,13 @@ class ProfScope {
   hipStream_t s_ = nullptr;
   double work_ = 0.0;
 };
+
+// mo_muon_step over a caller's workspace (mo_muon_step) or the library's
+// own scratch (mo_muon_step_noalloc: ws_name names it in the error when the
+// matrices need more than it holds).
+int one_shot_step(const mo_tensor* tensors, int64_t count, int grad_dtype, int mom_dtype, int ns_dtype, float lr,
+                  float wd, float mu, int nesterov, int ns_steps, const float* abc, float rms_scale, float eps,
+                  float* update_rms, void* workspace, size_t workspace_bytes, void* stream,
+                  const char* ws_name);
 
 }  // namespace mo

@@ -711,6 +711,35 @@ Hyper make_hyper(float lr, float wd, float mu, int nesterov, int ns_steps, const
 
 }  // namespace
 
+namespace mo {
+
+int one_shot_step(const mo_tensor* tensors, int64_t count, int grad_dtype, int mom_dtype, int ns_dtype, float lr,
+                  float wd, float mu, int nesterov, int ns_steps, const float* abc, float rms_scale, float eps,
+                  float* update_rms, void* workspace, size_t workspace_bytes, void* stream,
+                  const char* ws_name) {
+  HostPlan p;
+  int rc = build_plan(tensors, count, grad_dtype, mom_dtype, ns_dtype, true, p);
+  if (rc) return rc;
+  const Hyper h = make_hyper(lr, wd, mu, nesterov, ns_steps, abc, rms_scale, eps, true);
+  if ((rc = validate_hyper(h))) return rc;
+  if (update_rms && (reinterpret_cast<uintptr_t>(update_rms) & 3u))
+    return fail(MO_EINVAL, "update_rms must be 4-byte aligned");
+  if (count == 0) return MO_OK;
+  size_t full = 0, mn = 0;
+  ws_sizes(p, true, &full, &mn);
+  if (ws_name && mn > workspace_bytes)
+    return fail(MO_EWORKSPACE, "these matrices need %zu bytes of %s, more than its %zu bytes", mn, ws_name,
+                workspace_bytes);
+  if ((rc = check_workspace(workspace, workspace_bytes, mn))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((rc = upload_descs(p, ws, s))) return rc;
+  const size_t table = align_up(p.descs.size() * sizeof(MatDesc));
+  return run_step(p, reinterpret_cast<const MatDesc*>(ws), h, update_rms, ws, workspace_bytes, table, s, nullptr, 0);
+}
+
+}  // namespace mo
+
 struct mo_muon_plan {
   HostPlan plan;
   MatDesc* d_desc = nullptr;
@@ -738,22 +767,8 @@ int mo_muon_workspace_size(const mo_tensor* tensors, int64_t count, int ns_dtype
 int mo_muon_step(const mo_tensor* tensors, int64_t count, int grad_dtype, int mom_dtype, int ns_dtype, float lr,
                  float wd, float mu, int nesterov, int ns_steps, const float* abc, float rms_scale, float eps,
                  float* update_rms, void* workspace, size_t workspace_bytes, void* stream) {
-  HostPlan p;
-  int rc = build_plan(tensors, count, grad_dtype, mom_dtype, ns_dtype, true, p);
-  if (rc) return rc;
-  const Hyper h = make_hyper(lr, wd, mu, nesterov, ns_steps, abc, rms_scale, eps, true);
-  if ((rc = validate_hyper(h))) return rc;
-  if (update_rms && (reinterpret_cast<uintptr_t>(update_rms) & 3u))
-    return fail(MO_EINVAL, "update_rms must be 4-byte aligned");
-  if (count == 0) return MO_OK;
-  size_t full = 0, mn = 0;
-  ws_sizes(p, true, &full, &mn);
-  if ((rc = check_workspace(workspace, workspace_bytes, mn))) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if ((rc = upload_descs(p, ws, s))) return rc;
-  const size_t table = align_up(p.descs.size() * sizeof(MatDesc));
-  return run_step(p, reinterpret_cast<const MatDesc*>(ws), h, update_rms, ws, workspace_bytes, table, s, nullptr, 0);
+  return mo::one_shot_step(tensors, count, grad_dtype, mom_dtype, ns_dtype, lr, wd, mu, nesterov, ns_steps, abc,
+                           rms_scale, eps, update_rms, workspace, workspace_bytes, stream, nullptr);
 }
 
 int mo_muon_plan_create(const mo_tensor* tensors, int64_t count, int grad_dtype, int mom_dtype, int ns_dtype,
