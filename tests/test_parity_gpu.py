@@ -570,3 +570,43 @@ def test_steps_on_two_streams_use_separate_workspaces(mod):
         for got, want in zip(Pa + Ma + Pb + Mb, ref[0][0] + ref[0][1] + ref[1][0] + ref[1][1]):
             assert torch.equal(got, want)
 
+
+
+
+RAGGED_SHAPES = [(1408, 2048), (2048, 1408), (300, 700), (700, 300), (640, 900), (384, 1024)]
+
+
+@pytest.mark.parametrize("variant", [{}, {"ns_steps": 0}, {"ns_steps": 1}, {"waves": "4"}, {"c0": True},
+                                     {"scaling": "update_norm"}])
+def test_half_empty_last_panel(mod, monkeypatch, variant):
+    """Short sides that fill only half of their last 256-row panel (the MoE
+    experts' 1408 = 5.5 x 256; 300, 640, 384), both orientations, through a
+    plan: 4 waves, no quintic term (the polynomial reading S in its
+    epilogue), the update-norm scaling (the RMS-only pass), N = 0 and 1.
+    Each matrix against the oracle: update, momentum, update RMS, and the
+    per-singular-value deviation at N = 5."""
+    if variant.get("waves"):
+        monkeypatch.setenv("MO_WAVES", variant["waves"])
+    hyp = dict(HYP, ns_steps=variant.get("ns_steps", 5))
+    abc = (1.5, -0.5, 0.0) if variant.get("c0") else None
+    scaling = variant.get("scaling", "shape")
+    Ps, Gs, Ms = _mixed_state(1500, RAGGED_SHAPES)
+    P0, G0, M0 = [f64(p) for p in Ps], [f64(g) for g in Gs], [f64(m) for m in Ms]
+    rms = torch.full((len(Ps),), -1.0, device=DEV)
+    plan = mod.MuonPlan(Ps, Gs, Ms)
+    plan.step(update_rms=rms, scaling=scaling, abc=abc, **hyp)
+    torch.cuda.synchronize()
+    plan.close()
+    for i, s in enumerate(RAGGED_SHAPES):
+        Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=abc or mo.NS_COEFFS, scaling=scaling, **hyp)
+        err = sp.rel_fro(P0[i] - f64(Ps[i]), P0[i] - Wo)
+        print(s, variant, f"update rel_fro {err:.3e}")
+        assert err <= 2e-2, (s, err)
+        tol = np.abs(Mo) * (2.0 ** -8 + 2.0 ** -20) + (np.abs(0.95 * M0[i]) + np.abs(G0[i])) * 2.0 ** -22 + 1e-30
+        assert np.all(np.abs(f64(Ms[i]) - Mo) <= tol)
+        assert abs(rms[i].item() - rms_o) <= 2e-2 * rms_o
+        if hyp["ns_steps"] == 5 and abc is None and scaling == "shape":
+            r, c = s
+            X_rec = (P0[i] - f64(Ps[i]) - hyp["lr"] * hyp["wd"] * P0[i]) / (hyp["lr"] * 0.2 * math.sqrt(max(r, c)))
+            _, N = mo.momentum_update(M0[i], G0[i], 0.95, True)
+            assert sp.per_sigma_deviation(X_rec, N, 5, eps=1e-7) <= 0.05
