@@ -130,8 +130,18 @@ struct HostPlan {
 
 int dt_size(int dt) { return dt == F32 ? 4 : 2; }
 
-// Tile choice for a shape group: estimated time of the padded work, scaled
-// by a per-tile efficiency and by how well the update GEMM fills 256 CUs.
+// Tile choice for a shape group: the estimated time of its padded work at
+// each tile size.  The symmetric products (Gram and polynomial, lower tiles
+// only) and the update (all tiles) are separate launches, so each is charged
+// for how well its own tile count fills 256 CUs.  Per-tile efficiencies are
+// measured: with the chip filled, a 128 tile delivers about 0.75 and a 64
+// tile about 0.5 of a 256 tile's rate (Newton-Schulz alone, bf16, N = 5, 15
+// shapes from [64, 2048] to [2048, 5632] and batches of 8 to 64, every tile
+// size forced in turn); these constants pick the fastest size on 13 of the
+// 15 and lose 1.6% and 4.9% on the other two.  Groups of small matrices
+// (m <= 128, bf16, at least kSmallMinCount of them) take 128 tiles: the
+// fused small-matrix kernel works on 128-row panels.
+constexpr int kSmallMinCount = 32;
 TileCfg choose_tile(int m, int n, int count, int ns_dt) {
   if (const char* e = std::getenv("MO_TILE")) {
     const int t = std::atoi(e);
@@ -139,21 +149,22 @@ TileCfg choose_tile(int m, int n, int count, int ns_dt) {
     if (t == 128) return TILE_128;
     if (t == 64) return TILE_64;
   }
+  if (ns_dt == BF16 && m <= 128 && count >= kSmallMinCount) return TILE_128;
   const TileCfg cands_bf[] = {TILE_256, TILE_128, TILE_64};
   const TileCfg cands_f[] = {TILE_128, TILE_64};
   const TileCfg* c = ns_dt == BF16 ? cands_bf : cands_f;
   const int nc = ns_dt == BF16 ? 3 : 2;
+  auto filled = [](double tiles) { return tiles / (std::ceil(tiles / 256.0) * 256.0); };
   double best = 1e300;
   TileCfg pick = c[nc - 1];
   for (int i = 0; i < nc; ++i) {
     const int T = tile_size(c[i]);
-    const double eff = T == 256 ? 1.0 : (T == 128 ? 0.7 : 0.35);
+    const double eff = T == 256 ? 1.0 : (T == 128 ? 0.75 : 0.5);
     const double mp = static_cast<double>(ru(m, T)), np = static_cast<double>(ru(n, T));
-    const double work = 3.0 * mp * mp * np + mp * mp * mp;
-    const double tiles = static_cast<double>(count) * (mp / T) * (np / T);
-    const double waves = std::ceil(tiles / 256.0);
-    const double fill = tiles / (waves * 256.0);
-    const double cost = work * count / (eff * fill);
+    const double tm = mp / T, tn = np / T;
+    const double sym_work = (mp * mp * np + mp * mp * mp) * count;
+    const double upd_work = 2.0 * mp * mp * np * count;
+    const double cost = (sym_work / filled(count * tm * (tm + 1) / 2) + upd_work / filled(count * tm * tn)) / eff;
     if (cost < best * 0.999) {
       best = cost;
       pick = c[i];
@@ -499,7 +510,6 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
 // general kernels).  The choice depends on the whole group, not on the
 // chunk a smaller workspace processes at a time, so results do not depend
 // on the workspace size.
-constexpr int kSmallMinCount = 32;
 bool small_eligible(const StepCtx& c, const Item& it) {
   const char* e = std::getenv("MO_NO_SMALL");
   const bool off = e && std::atoi(e) != 0;
