@@ -168,15 +168,20 @@ def measured_peaks():
         return None
     L = ctypes.CDLL(path)
     L.mo_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    L.mo_probe_mfma_bf16_random.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     L.mo_probe_hbm.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                ctypes.POINTER(ctypes.c_double)]
-    tf, rd, cp = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    tf, tr, rd, cp = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     if L.mo_probe_mfma_bf16(20000, 3, ctypes.byref(tf)) != 0:
+        return None
+    if L.mo_probe_mfma_bf16_random(20000, 3, ctypes.byref(tr)) != 0:
         return None
     if L.mo_probe_hbm(4 << 30, 3, ctypes.byref(rd), ctypes.byref(cp)) != 0:
         return None
-    return {"bf16_mfma_tflops": tf.value, "hbm_read_gbs": rd.value, "hbm_copy_gbs": cp.value,
-            "method": "register-only v_mfma_f32_32x32x16_bf16 loop, 2 waves per SIMD on every CU; "
+    return {"bf16_mfma_tflops": tf.value, "bf16_mfma_random_tflops": tr.value,
+            "hbm_read_gbs": rd.value, "hbm_copy_gbs": cp.value,
+            "method": "register-only v_mfma_f32_32x32x16_bf16 loop, 2 waves per SIMD on every CU, on "
+                      "near-constant operands and on random bf16 operands cycled per instruction; "
                       "4 GiB read-only and copy streams (copy counts read + write)"}
 
 
@@ -350,6 +355,8 @@ def main():
         if peaks and wl.ns_dtype == torch.bfloat16:
             roofline["measured_peak"] = peaks["bf16_mfma_tflops"]
             roofline["frac_of_measured_peak"] = ach / peaks["bf16_mfma_tflops"]
+            roofline["measured_peak_random_operands"] = peaks["bf16_mfma_random_tflops"]
+            roofline["frac_of_measured_peak_random_operands"] = ach / peaks["bf16_mfma_random_tflops"]
     if peaks:
         for k in kernels.values():
             if k["unit"] == "GB/s":

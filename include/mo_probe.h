@@ -30,10 +30,22 @@ extern "C" {
  * *tflops = 32768 flop x MFMAs / seconds; best of `reps` launches. */
 int mo_probe_mfma_bf16(int iters, int reps, double* tflops);
 
+/* The same grid and issue pattern on operands that switch like a product of
+ * random matrices: each lane cycles through eight A and eight B register
+ * operands of random bf16 values (random sign and mantissa, magnitudes
+ * 2^-8 .. 1), so consecutive MFMAs never see the same inputs.  The
+ * constant-like operands of mo_probe_mfma_bf16 toggle few bits; this rate
+ * is what the matrix cores sustain within the chip's power budget on real
+ * data, still with no memory traffic.  Same units and outputs. */
+int mo_probe_mfma_bf16_random(int iters, int reps, double* tflops);
+
 /* HBM rates over a buffer of `bytes` (rounded down to 64 KiB):
  * *read_gbs: a read-only reduction of the whole buffer (16-byte loads);
  * *copy_gbs: a copy into a second buffer, counted as read + write bytes.
- * Best of `reps` launches each. */
+ * Each stream runs in four launch shapes (1, 2 or 4 loads in flight per
+ * thread; 4 to 64 workgroups of 256 threads per CU), since the fastest
+ * shape differs from box to box by 10-20%; the best of `reps` launches of
+ * every shape is reported. */
 int mo_probe_hbm(size_t bytes, int reps, double* read_gbs, double* copy_gbs);
 
 /* Message of the last failure on this thread. */

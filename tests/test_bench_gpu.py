@@ -55,6 +55,8 @@ def test_bench_default_line():
     pk = d["measured_peaks"]
     assert 500 < pk["bf16_mfma_tflops"] < 2600 and 1000 < pk["hbm_read_gbs"] < 9000
     assert 0 < d["roofline"]["frac_of_measured_peak"] < 1.2
+    assert 500 < pk["bf16_mfma_random_tflops"] <= 1.05 * pk["bf16_mfma_tflops"]
+    assert 0 < d["roofline"]["frac_of_measured_peak_random_operands"] < 1.2
 
 
 def test_bench_800m_line():
