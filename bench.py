@@ -363,6 +363,7 @@ def main():
                 k["frac_of_measured_copy"] = k["rate"] / peaks["hbm_copy_gbs"]
     ew_bytes = wl.n_elems * W.muon_elementwise_bytes_per_elem(wl) + \
         (wl.n_vec_elems * W.ADAMW_BYTES_PER_ELEM if wl.vecs else 0)
+    ideal_ms = (alg_flops / (peak * 1e12) + ew_bytes / (HBM_PEAK_GBS * 1e9)) * 1e3
     line = {
         "metric": "Muon optimizer steps/s + Newton-Schulz TFLOP/s (% bf16 MFMA peak) per config",
         "value": steps_per_s, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -374,7 +375,10 @@ def main():
                    "muon_elements": wl.n_elems, "adamw_elements": wl.n_vec_elems,
                    "ns_steps": wl.ns_steps, "scaling": args.scaling,
                    "grad_dtype": str(wl.grad_dtype).split(".")[-1],
-                   "mom_dtype": str(wl.mom_dtype).split(".")[-1]},
+                   "mom_dtype": str(wl.mom_dtype).split(".")[-1],
+                   "seeds": {"weights": W.seed_of(wl.cid, 0), "grads": W.seed_of(wl.cid, 1),
+                             "rule": "workload id x 1e6 + tensor kind x 1e4 + step "
+                                     "(kinds: 0 W, 1 G, 2 M, 3 scales, 4 AdamW W, 5 AdamW g)"}},
         "matrices_per_s": wl.n_mats * steps_per_s,
         "ns_alg_tflop_per_step": alg_flops / 1e12,
         "ns_tflops": (alg_flops / (ns_ms * 1e-3) / 1e12) if ns_ms > 0 else None,
@@ -382,6 +386,10 @@ def main():
         "ns_ms_per_step": ns_ms,
         "step_tflops_wallclock": alg_flops / (ms_per_step * 1e-3) / 1e12,
         "elementwise_alg_gb_per_step": ew_bytes / 1e9,
+        # the step at the datasheet roofline: products at the MFMA peak,
+        # momentum/apply/AdamW bytes at 8 TB/s
+        "ideal_step_ms": ideal_ms,
+        "frac_of_ideal_step_rate": ideal_ms / ms_per_step,
         "kernels": kernels,
         "roofline": roofline,
         "measured_peaks": peaks,

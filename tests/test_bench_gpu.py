@@ -57,6 +57,11 @@ def test_bench_default_line():
     assert 0 < d["roofline"]["frac_of_measured_peak"] < 1.2
     assert 500 < pk["bf16_mfma_random_tflops"] <= 1.05 * pk["bf16_mfma_tflops"]
     assert 0 < d["roofline"]["frac_of_measured_peak_random_operands"] < 1.2
+    # the datasheet-roofline step: 1.187e15 flops at 2516.6 TFLOP/s plus 8.59e9
+    # elements x 16 B at 8 TB/s
+    assert abs(d["ideal_step_ms"] - (1.187e15 / 2516.6e12 + 8.59e9 * 16 / 8e12) * 1e3) < 2.0
+    assert 0 < d["frac_of_ideal_step_rate"] < 1
+    assert d["config"]["seeds"]["grads"] == 5 * 1_000_000 + 10_000
 
 
 def test_bench_800m_line():
