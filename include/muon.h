@@ -60,6 +60,11 @@
  *              MO_NO_SMALL=1       run groups of small matrices (m <= 128)
  *                                  through the per-product kernels instead
  *                                  of the fused one.
+ *            Groups of at least 32 bf16 matrices with m <= 128 take a fused
+ *            kernel that iterates on the m x m Gram matrix at about fp32
+ *            precision (ns_steps <= 5; longer iterations take the
+ *            per-product kernels): its results are more accurate than the
+ *            bf16 iterates of the per-product kernels, not bitwise equal.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H

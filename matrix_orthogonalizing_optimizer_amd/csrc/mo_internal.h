@@ -100,7 +100,7 @@ struct GemmArgs {
 // panels): one workgroup per matrix (ns_small.hip).
 struct SmallBin {
   const MatDesc* desc;                   // per matrix
-  void* x0; void* x1;                    // X_0 (unscaled N) and the ping-pong buffer
+  const void* x0;                        // X_0 (unscaled N), blocked [128, n_pad]
   int64_t x_stride;                      // elements per matrix: 128 * n_pad
   const float* rscale;                   // 1 / (||N||_F + eps) per matrix
   float* rms_part;                       // [count][n_pad / 128] or null

@@ -507,14 +507,22 @@ int gemm_phase(const StepCtx& c, std::vector<Item>& items, Epi epi, int k, int c
 // on one 128-row panel (m <= 128, bf16) and are numerous enough to fill the
 // chip with one workgroup each; it applies with the shape or hidden scaling
 // (the update-norm scaling and the Newton-Schulz-only entry point take the
-// general kernels).  The choice depends on the whole group, not on the
-// chunk a smaller workspace processes at a time, so results do not depend
-// on the workspace size.
+// general kernels).  It iterates on the m x m Gram matrix, where rounding
+// can push the eigenvalues of directions with tiny singular values below
+// zero; the polynomial then amplifies them by about a^2 = 11.9 per step
+// without the bound that the odd polynomial keeps on singular values.  Up
+// to 5 steps this stays at or below the error of bf16 iterates even on
+// rank-deficient inputs; from 8 steps on it can overflow, so longer
+// iterations take the general kernels.  The choice depends on the whole
+// group, not on the chunk a smaller workspace processes at a time, so
+// results do not depend on the workspace size.
+constexpr int kSmallMaxSteps = 5;
 bool small_eligible(const StepCtx& c, const Item& it) {
   const char* e = std::getenv("MO_NO_SMALL");
   const bool off = e && std::atoi(e) != 0;
   return !off && c.plan.ns_dt == BF16 && it.bin->cfg == TILE_128 && it.bin->m_pad == 128 &&
-         it.bin->count >= kSmallMinCount && c.store_out == nullptr && c.h.scaling != MO_SCALE_UPDATE_NORM;
+         it.bin->count >= kSmallMinCount && c.store_out == nullptr && c.h.scaling != MO_SCALE_UPDATE_NORM &&
+         c.h.ns_steps <= kSmallMaxSteps;
 }
 
 // Momentum, norm, Newton-Schulz and apply for a set of items processed
@@ -604,7 +612,7 @@ int run_round(const StepCtx& c, std::vector<Item>& items) {
         const Item& it = small[j];
         SmallBin& sb = a.bin[a.nbins++];
         sb.desc = it.desc;
-        sb.x0 = it.x[0]; sb.x1 = it.x[1];
+        sb.x0 = it.x[0];
         sb.x_stride = it.L.x_elems;
         sb.rscale = it.rscale;
         sb.rms_part = want_rms ? it.rms_part : nullptr;

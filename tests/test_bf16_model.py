@@ -28,6 +28,12 @@ stored iterate to bf16 -- not from the kernels -- and this model shows it:
 * the model itself, with rounding switched off, agrees with the fp64
   oracle to fp32 accuracy, and its N = 5 errors on the workload shapes
   are ~0.8-0.9e-2, matching the GPU's.
+
+The fused small-matrix path (groups of m <= 128 matrices) does not form
+bf16 iterates: it iterates on the m x m Gram matrix with split-bf16
+products (``bf16_model.ns_gram_space``).  Its tests below pin that model to
+the oracle on exact inputs, give its error on Gaussian inputs (the bf16
+storage of X_0, ~1.7-2.1e-3) and show why the path stops at N = 5.
 """
 
 from __future__ import annotations
@@ -141,3 +147,87 @@ def test_full_size_n10_figures(shape):
           f"worst at x0 {x0[dev.argmax()]:.4f}")
     assert 2.0e-2 <= e <= 2.5e-2
     assert 0.035 <= resolved <= 0.06
+
+
+# ---- the fused small-matrix path (m <= 128): iteration in Gram space
+
+@pytest.mark.parametrize("shape", [(96, 300), (300, 96), (128, 2048), (17, 40), (128, 128)])
+def test_gram_space_model_on_exact_inputs(shape):
+    """With a bf16-representable input (X_0 = N exactly) only the split
+    products round: the Gram-space recursion reproduces the iteration to
+    ~1e-5 (a wrong recursion -- S_{k+1} = P S, a dropped r -- is off by
+    O(1), next test).  The square shape's smallest directions make it the
+    worst case (3e-4 at N = 5)."""
+    x = bm.to_bf16(_randn(shape, 3 + shape[0]).astype(np.float32)).astype(np.float64)
+    for steps in (1, 2, 3, 5):
+        ref, _ = mo.orthogonalize(x, steps)
+        bound = 1e-4 if shape != (128, 128) else (1e-4 if steps <= 2 else 1e-3)
+        assert sp.rel_fro(bm.ns_gram_space(x, steps), ref) <= bound, (shape, steps)
+
+
+def test_gram_space_model_wrong_recursions_fail():
+    x = bm.to_bf16(_randn((96, 300), 99).astype(np.float32)).astype(np.float64)
+    ref, _ = mo.orthogonalize(x, 5)
+    a, b, c = mo.NS_COEFFS
+    r = 1.0 / np.sqrt(np.sum(x * x))
+    S = r * r * (x @ x.T)
+    eye = np.eye(96)
+    Q1, Q2, S1, S2 = eye, eye, S.copy(), S.copy()
+    for _ in range(5):
+        P1 = a * eye + b * S1 + c * S1 @ S1
+        S1, Q1 = P1 @ S1, P1 @ Q1              # S_{k+1} = P S: one factor of P dropped
+        P2 = a * eye + b * S2 + c * S2 @ S2
+        S2, Q2 = P2 @ S2 @ P2, P2 @ Q2
+    assert sp.rel_fro(r * Q2 @ x, ref) <= 1e-9            # the exact recursion
+    assert sp.rel_fro(r * Q1 @ x, ref) >= 0.1
+    assert sp.rel_fro(Q2 @ x, ref) >= 0.1                 # r not applied to X_0
+
+
+@pytest.mark.parametrize("shape", [(128, 2048), (2048, 128), (128, 512), (700, 96), (100, 300), (96, 300),
+                                   (128, 128)])
+def test_gram_space_model_accuracy(shape):
+    """On Gaussian inputs the Gram-space path's error is the bf16 storage
+    of X_0 (~1.7e-3), 3-5x below the bf16 iterates of the general path at
+    N = 5: at most 2.1e-3 Frobenius off the square shape (3.2e-3 on
+    [128, 128]); per-sigma at most 7e-4 (0.0045 on the square shape)."""
+    x = _randn(shape, 11 + shape[1])
+    sq = shape[0] == shape[1]
+    for steps in (1, 2, 5):
+        ref, _ = mo.orthogonalize(x, steps)
+        X = bm.ns_gram_space(x, steps)
+        fro, dev = sp.rel_fro(X, ref), sp.per_sigma_deviation(X, x, steps)
+        assert fro <= (3.5e-3 if sq else 2.5e-3), (shape, steps, fro)
+        assert dev <= (0.005 if sq else 0.001), (shape, steps, dev)
+        if steps == 5:
+            assert fro <= 0.5 * sp.rel_fro(bm.ns_bf16(x, steps), ref)
+
+
+def _spectrum_matrix(m, n, sig, seed):
+    rng = np.random.default_rng(seed)
+    U, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, m)))
+    return (U * sig) @ V.T
+
+
+@pytest.mark.parametrize("kind", ["rank half", "logspace 1..1e-6"])
+def test_gram_space_is_safe_to_five_steps_only(kind):
+    """Why the fused small-matrix path stops at N = 5.  On inputs with
+    (near-)zero singular values the Gram-space recursion's rounding can
+    make a tiny direction's eigenvalue of S negative; S -> P S P then grows
+    it by about a^2 per step with nothing to bound it (the odd polynomial
+    bounds singular values, not negative eigenvalues).  Up to N = 6 the
+    Gram-space error stays at or below that of bf16 iterates on such
+    inputs; at N = 8 it is orders of magnitude larger (bf16 iterates stay
+    bounded)."""
+    m, n = 128, 2048
+    sig = np.r_[np.ones(m // 2), np.zeros(m - m // 2)] if kind == "rank half" else np.logspace(0, -6, m)
+    x = _spectrum_matrix(m, n, sig, 5)
+    for steps in (3, 5, 6):
+        ref, _ = mo.orthogonalize(x, steps)
+        assert sp.rel_fro(bm.ns_gram_space(x, steps), ref) <= sp.rel_fro(bm.ns_bf16(x, steps), ref)
+    ref, _ = mo.orthogonalize(x, 8)
+    with np.errstate(over="ignore", invalid="ignore"):
+        gram = sp.rel_fro(bm.ns_gram_space(x, 8), ref)
+    bf16 = sp.rel_fro(bm.ns_bf16(x, 8), ref)
+    assert bf16 < 2.0
+    assert not np.isfinite(gram) or gram > 10.0 * bf16

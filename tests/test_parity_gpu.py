@@ -320,9 +320,14 @@ def test_step_alternative_scalings(mod, monkeypatch, scaling, ns_steps, tile):
 @pytest.mark.parametrize("scaling", ["shape", "hidden"])
 def test_small_matrix_fused_path(mod, ns_steps, scaling):
     """Shape groups of >= 32 matrices with m <= 128 take the fused kernel
-    (all iterations and the apply in one workgroup per matrix): ragged and
+    (the iteration carried out on m x m matrices at about fp32 precision,
+    then X_N = Q X_0 and the apply, one workgroup per matrix): ragged and
     oriented shapes, sampled matrices against the oracle, update RMS of
-    every matrix."""
+    every matrix.  Its error is the bf16 storage of X_0, as in the CPU model
+    ``bf16_model.ns_gram_space`` (test_bf16_model.py): off the square shape
+    the bounds are that model's figures with a margin (1.6-2.1e-3 Frobenius
+    measured at N <= 5), well inside the bf16 bar and at N = 10 below what
+    bf16 iterates reach."""
     groups = [((128, 512), 32), ((700, 96), 33), ((100, 300), 34), ((128, 128), 32)]
     shapes = [s for s, n in groups for _ in range(n)]
     Ps, Gs, Ms = _mixed_state(1300 + ns_steps, shapes)
@@ -342,23 +347,66 @@ def test_small_matrix_fused_path(mod, ns_steps, scaling):
                                              hidden=512.0, **hyp)
             P1, M1 = f64(Ps[i]), f64(Ms[i])
             err = sp.rel_fro(P0[i] - P1, P0[i] - Wo)
-            print(shp, ns_steps, scaling, f"update rel_fro {err:.3e}")
-            assert err <= 2e-2, (shp, i, err)
+            r, cc = shp
+            sq = r == cc
+            scale = 0.2 * (math.sqrt(512.0) if scaling == "hidden" else math.sqrt(max(r, cc)))
+            X_rec = (P0[i] - P1 - 1e-3 * 0.1 * P0[i]) / (1e-3 * scale)
+            _, N = mo.momentum_update(M0[i], G0[i], 0.95, True)
+            dev = sp.per_sigma_deviation(X_rec, N, ns_steps, eps=1e-7)
+            print(shp, ns_steps, scaling, f"update rel_fro {err:.3e}, per-sigma {dev:.4f}")
+            if sq:
+                # a square matrix's smallest singular values are tiny and
+                # vary from matrix to matrix; the m x m recursion amplifies
+                # their rounding as bf16 iterates do (per-sigma 0.015 on one
+                # [128, 128] matrix at N = 5): the bf16 bars
+                assert err <= 1e-2, (shp, i, err)
+                assert dev <= 0.05, (shp, i, dev)
+            else:
+                assert err <= 4e-3, (shp, i, err)
+                assert dev <= 0.002, (shp, i, dev)
             tol = np.abs(Mo) * (2.0 ** -8 + 2.0 ** -20) + (np.abs(0.95 * M0[i]) + np.abs(G0[i])) * 2.0 ** -22 + 1e-30
             assert np.all(np.abs(M1 - Mo) <= tol)
             assert abs(rms[i].item() - rms_o) <= 2e-2 * rms_o
-            if ns_steps == 5 and min(shp) > 1:
-                r, cc = shp
-                scale = 0.2 * (math.sqrt(512.0) if scaling == "hidden" else math.sqrt(max(r, cc)))
-                X_rec = (P0[i] - P1 - 1e-3 * 0.1 * P0[i]) / (1e-3 * scale)
-                _, N = mo.momentum_update(M0[i], G0[i], 0.95, True)
-                assert sp.per_sigma_deviation(X_rec, N, 5, eps=1e-7) <= 0.05
         start += n
 
 
+def test_small_group_beyond_five_steps_takes_general_kernels(mod, monkeypatch):
+    """N = 10 on groups that would otherwise take the fused kernel: the
+    Gram-space recursion is not used past 5 steps (rounding can turn a tiny
+    direction's Gram eigenvalue negative, and the polynomial grows it
+    without bound), so the per-product kernels run and the bf16 N = 10
+    figures apply: per-sigma <= 0.05 and Frobenius well inside 4e-2 on
+    rectangular shapes.  Their bitwise equality with MO_NO_SMALL=1 shows
+    that the fused kernel was not used."""
+    groups = [((128, 512), 32), ((700, 96), 33)]
+    shapes = [s for s, n in groups for _ in range(n)]
+    outs = []
+    for off in ("0", "1"):
+        monkeypatch.setenv("MO_NO_SMALL", off)
+        Ps, Gs, Ms = _mixed_state(1500, shapes)
+        P0 = [f64(p) for p in Ps]
+        M0 = [f64(m) for m in Ms]
+        G0 = [f64(g) for g in Gs]
+        mod.muon_step(Ps, Gs, Ms, **dict(HYP, ns_steps=10))
+        torch.cuda.synchronize()
+        outs.append([f64(p) for p in Ps])
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    for i in (0, 31, 32, len(shapes) - 1):
+        Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=mo.NS_COEFFS, **dict(HYP, ns_steps=10))
+        err = sp.rel_fro(P0[i] - outs[0][i], P0[i] - Wo)
+        r, cc = shapes[i]
+        X_rec = (P0[i] - outs[0][i] - 1e-3 * 0.1 * P0[i]) / (1e-3 * 0.2 * math.sqrt(max(r, cc)))
+        _, N = mo.momentum_update(M0[i], G0[i], 0.95, True)
+        dev = sp.per_sigma_deviation(X_rec, N, 10, eps=1e-7)
+        print(shapes[i], f"N = 10 update rel_fro {err:.3e}, per-sigma {dev:.4f}")
+        assert err <= 4e-2 and dev <= 0.05, (shapes[i], err, dev)
+
+
 def test_small_fused_matches_general_path(mod, monkeypatch):
-    """The fused kernel and the per-product kernels agree on the same step
-    to bf16 rounding (the iterates are rounded at the same points)."""
+    """The fused kernel (Gram-space iteration, about fp32 precision) and the
+    per-product kernels (bf16 iterates) agree on the same step to within the
+    bf16 path's own error (~8e-3 against the oracle at this shape, N = 5)."""
     shapes = [(128, 2048)] * 40
     outs = []
     for off in ("0", "1"):
