@@ -65,6 +65,10 @@ def measured_traffic(name: str, match):
     return b / n if n else None
 
 
+def _is_small_kernel(name: str) -> bool:
+    return name.startswith("mo::ns_small_kernel")
+
+
 def _is_update_gemm(name: str) -> bool:
     # mo::ns_gemm_kernel<T, TILE, EPI, WAVES>, EPI 2 = the update product
     targs = name[name.find("<") + 1:name.rfind(">")].split(",")
@@ -346,7 +350,24 @@ def main():
     upd = prof["update"]
     peaks = None if args.no_probe else measured_peaks()
     roofline = None
-    if upd[0]:
+    # groups of small matrices (m <= 128) run one fused kernel per step,
+    # recorded as the update class with no Gram, polynomial or apply
+    # launches; it moves X_0 twice (bf16) and W in and out (fp32) and is
+    # bound by HBM, not by the matrix cores
+    fused_small = upd[0] > 0 and prof["gram"][0] == 0 and prof["apply"][0] == 0
+    if fused_small and wl.ns_dtype == torch.bfloat16:
+        fbytes = wl.n_elems * (2 * 2 + 8) * args.steps          # over the timed steps
+        ach = fbytes / (upd[1] * 1e-3) / 1e9
+        kernels["update"]["hbm_gb_per_s"] = ach
+        roofline = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl.key, _is_small_kernel),
+                    "kernel": "ns_small fused Newton-Schulz + apply (Gram-space iteration)",
+                    "bytes_per_launch": fbytes / upd[0], "mean_launch_ms": upd[1] / upd[0],
+                    "alg_tflops": upd[2] / (upd[1] * 1e-3) / 1e12}
+        if peaks:
+            roofline["measured_peak"] = peaks["hbm_copy_gbs"]
+            roofline["frac_of_measured_peak"] = ach / peaks["hbm_copy_gbs"]
+    elif upd[0]:
         ach = upd[2] / (upd[1] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                     "frac": ach / peak, "traffic": measured_traffic(wl.key, _is_update_gemm),

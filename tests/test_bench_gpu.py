@@ -71,6 +71,18 @@ def test_bench_800m_line():
     assert "[32000, 1536]" in d["cpu_baseline"]["sample"]
 
 
+def test_bench_small_matrix_line():
+    """The per-head workload runs the fused small-matrix kernel, which is
+    bound by HBM: its roofline is GB/s over X_0 read twice and W read and
+    written (12 bytes per element)."""
+    d = _run(["--workload", "kv_heads", "--steps", "3", "--warmup", "1", "--no-probe", "--no-cpu-baseline"])
+    _check_common(d, 3, 1)
+    roof = d["roofline"]
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and "ns_small" in roof["kernel"]
+    assert abs(roof["bytes_per_launch"] - 960 * 128 * 2048 * 12) < 1.0
+    assert set(d["kernels"]) >= {"momentum", "update"} and "gram" not in d["kernels"]
+
+
 def test_bench_svd_entropy_line():
     d = _run(["--svd-entropy", "--workload", "llama1p5b_gqa", "--steps", "1", "--warmup", "0",
               "--no-cpu-baseline"])
