@@ -370,6 +370,39 @@ def test_small_matrix_fused_path(mod, ns_steps, scaling):
         start += n
 
 
+def test_small_fused_edge_shapes(mod):
+    """Fused small-matrix kernel on the edges of its domain: one-row and
+    one-column matrices, a 5 x 7 matrix (both sides far below one 128
+    panel), and zero gradients with zero momentum in the middle of a group
+    (X_N = 0: a decay-only step and an update RMS of 0)."""
+    groups = [((1, 300), 32), ((300, 1), 32), ((5, 7), 32), ((64, 200), 33)]
+    shapes = [s for s, n in groups for _ in range(n)]
+    Ps, Gs, Ms = _mixed_state(1600, shapes)
+    zero = [len(shapes) - 10, len(shapes) - 9]
+    for i in zero:
+        Gs[i].zero_()
+        Ms[i].zero_()
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    rms = torch.zeros(len(shapes), device=DEV)
+    plan = mod.MuonPlan(Ps, Gs, Ms)
+    plan.step(update_rms=rms, **HYP)
+    torch.cuda.synchronize()
+    plan.close()
+    for i in [0, 31, 32, 63, 64, 95, 96, len(shapes) - 1] + zero:
+        P1 = f64(Ps[i])
+        if i in zero:
+            assert np.allclose(P1, P0[i] * (1 - HYP["lr"] * HYP["wd"]), rtol=1e-6, atol=0)
+            assert rms[i].item() == 0.0
+            continue
+        Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=mo.NS_COEFFS, **HYP)
+        err = sp.rel_fro(P0[i] - P1, P0[i] - Wo)
+        print(shapes[i], f"update rel_fro {err:.3e}")
+        assert err <= 4e-3, (shapes[i], i, err)
+        assert abs(rms[i].item() - rms_o) <= 2e-2 * rms_o
+
+
 def test_small_group_beyond_five_steps_takes_general_kernels(mod, monkeypatch):
     """N = 10 on groups that would otherwise take the fused kernel: the
     Gram-space recursion is not used past 5 steps (rounding can turn a tiny
