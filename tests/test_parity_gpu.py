@@ -403,6 +403,26 @@ def test_small_fused_edge_shapes(mod):
         assert abs(rms[i].item() - rms_o) <= 2e-2 * rms_o
 
 
+@pytest.mark.parametrize("abc,steps", [((1.5, -0.5, 0.0), 3), ((2.0, -1.5, 0.5), 4)])
+def test_small_fused_custom_coefficients(mod, abc, steps):
+    """Custom Eq. 2 coefficients through the fused kernel: the cubic
+    (c = 0, P = a I + b S) and another quintic, against the oracle with
+    the same coefficients, off the default five steps."""
+    shapes = [(100, 300)] * 33 + [(256, 64)] * 32
+    Ps, Gs, Ms = _mixed_state(1700, shapes)
+    P0 = [f64(p) for p in Ps]
+    M0 = [f64(m) for m in Ms]
+    G0 = [f64(g) for g in Gs]
+    hyp = dict(HYP, ns_steps=steps)
+    mod.muon_step(Ps, Gs, Ms, abc=abc, **hyp)
+    torch.cuda.synchronize()
+    for i in (0, 32, 33, len(shapes) - 1):
+        Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0[i], M0[i], abc=abc, **hyp)
+        err = sp.rel_fro(P0[i] - f64(Ps[i]), P0[i] - Wo)
+        print(shapes[i], abc, steps, f"update rel_fro {err:.3e}")
+        assert err <= 4e-3, (shapes[i], abc, err)
+
+
 def test_small_group_beyond_five_steps_takes_general_kernels(mod, monkeypatch):
     """N = 10 on groups that would otherwise take the fused kernel: the
     Gram-space recursion is not used past 5 steps (rounding can turn a tiny
