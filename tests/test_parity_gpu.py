@@ -423,6 +423,49 @@ def test_small_fused_custom_coefficients(mod, abc, steps):
         assert err <= 4e-3, (shapes[i], abc, err)
 
 
+def test_small_fused_ill_conditioned(mod, monkeypatch):
+    """Gram-space kernel on inputs where the m x m recursion is most
+    sensitive: rank-deficient gradients (rank 16 of 128) and spectra spread
+    over six decades, N = 5, zero momentum.  The fused kernel stays finite
+    and at least as close to the oracle as the bf16 iterates of the general
+    kernels (MO_NO_SMALL=1) on the same step -- the CPU model's finding in
+    test_bf16_model.py, here on the GPU."""
+    g = torch.Generator().manual_seed(1900)
+
+    def spectrum_matrix(m, n, sig):
+        U, _ = torch.linalg.qr(torch.randn(m, m, generator=g, dtype=torch.float64))
+        V, _ = torch.linalg.qr(torch.randn(n, m, generator=g, dtype=torch.float64))
+        return (U * torch.as_tensor(sig)) @ V.T
+
+    shapes, grads = [], []
+    for i in range(32):
+        sig = np.r_[np.ones(16), np.zeros(112)] * 1e-3
+        grads.append(spectrum_matrix(128, 512, sig))
+        shapes.append((128, 512))
+    for i in range(32):
+        grads.append(spectrum_matrix(128, 2048, np.logspace(0, -6, 128) * 1e-3))
+        shapes.append((128, 2048))
+    P_init = [torch.randn(s, generator=g).mul(0.02).to(DEV) for s in shapes]
+    outs = {}
+    for off in ("0", "1"):
+        monkeypatch.setenv("MO_NO_SMALL", off)
+        Ps = [p.clone() for p in P_init]
+        Gs = [x.float().to(DEV) for x in grads]
+        Ms = [torch.zeros(s, device=DEV, dtype=torch.bfloat16) for s in shapes]
+        mod.muon_step(Ps, Gs, Ms, **HYP)
+        torch.cuda.synchronize()
+        outs[off] = [f64(p) for p in Ps]
+    P0 = [f64(p) for p in P_init]
+    for i in (0, 31, 32, 63):
+        assert np.all(np.isfinite(outs["0"][i]))
+        G0 = f64(grads[i].float())
+        Wo, Mo, Xo, rms_o = mo.muon_step(P0[i], G0, np.zeros(shapes[i]), abc=mo.NS_COEFFS, **HYP)
+        e_fused = sp.rel_fro(P0[i] - outs["0"][i], P0[i] - Wo)
+        e_general = sp.rel_fro(P0[i] - outs["1"][i], P0[i] - Wo)
+        print(shapes[i], f"fused {e_fused:.3e}, general {e_general:.3e}")
+        assert e_fused <= e_general, (i, e_fused, e_general)
+
+
 def test_small_group_beyond_five_steps_takes_general_kernels(mod, monkeypatch):
     """N = 10 on groups that would otherwise take the fused kernel: the
     Gram-space recursion is not used past 5 steps (rounding can turn a tiny
