@@ -50,26 +50,34 @@ constexpr int kNT = 512;                // threads
 constexpr int kStage = kT * kCPR;       // chunks of one [128 rows][64 B] stage (8 KiB)
 constexpr int kSub = 2;                 // K-stages per ring slot (one barrier per slot)
 constexpr int kSlot = kSub * kStage;
-// A split m x m matrix is two arrays (hi, lo) of [128 rows][17 chunks]:
-// chunk 4 kb + lq of row r holds columns 32 kb + 4 lq + 0..3 and
-// 32 kb + 16 + 4 lq + 0..3 (8 bf16); the 17th chunk pads the row so that
-// 16 consecutive rows fall on distinct banks.
-constexpr int kPitch = 17;
-constexpr int kMat = kT * kPitch;       // chunks of one array
+// A split m x m matrix is two arrays (hi, lo) of [128 rows][16 chunks]:
+// logical chunk c = 4 kb + lq of row r holds columns 32 kb + 4 lq + 0..3
+// and 32 kb + 16 + 4 lq + 0..3 (8 bf16) and sits at position c ^ (r & 15)
+// of the row.  Reads of 16 rows x 4 chunks (the A fragments) and the
+// stores of a strip then fall on distinct banks; a row pitch of 17 chunks
+// (the usual pad) leaves the reads with two-way conflicts on gfx950.
+constexpr int kMat = kT * 16;           // chunks of one array (32 KiB)
 constexpr int kOffSh = 0, kOffSl = kMat;            // S
 constexpr int kOffPh = 2 * kMat, kOffPl = 3 * kMat; // P
 constexpr int kOffEnd = 4 * kMat;
 constexpr int kApLd = kT + 4;           // padded fp32 row (S_0 staging, apply staging)
+// fp32 [128][kApLd] staging (S_0 before the iteration, X_N tiles in the
+// apply) from the start of P on; it runs past the end of P.
+constexpr int kOffStage = kOffPh;
+constexpr int kStageChunks = kT * kApLd * 4 / 16;
+constexpr int kLdsChunks = kOffStage + kStageChunks > kOffEnd ? kOffStage + kStageChunks : kOffEnd;
 // X_0 streams through a ring of 16 KiB slots, all but one in flight: 8
-// slots over S and P while S_0 is accumulated, 4 over P in the last
-// product (the apply stages its tile over S meanwhile).  The fp32 S_0 is
-// staged over P.
+// slots over S and P while S_0 is accumulated, 4 over S in the last
+// product (the apply stages its tile above them meanwhile).  The fp32 S_0
+// is staged once the first ring has drained.
 constexpr int kNSTG = 8, kOffRingG = 0;
-constexpr int kNSTA = 4, kOffRingA = kOffPh;
+constexpr int kNSTA = 4, kOffRingA = 0;
 static_assert(kNSTG * kSlot <= kOffEnd, "S_0 ring fits over S and P");
-static_assert(kNSTA * kSlot <= 2 * kMat, "last ring fits over P");
-static_assert(kT * kApLd * 4 <= 2 * kMat * 16, "fp32 staging fits over one split matrix");
-static_assert(kOffEnd * 16 <= 160 * 1024, "LDS");
+static_assert(kOffRingA + kNSTA * kSlot <= kOffStage, "last ring fits below the staging");
+static_assert(kLdsChunks * 16 <= 160 * 1024, "LDS");
+
+// Position of logical chunk c of row r of a split matrix.
+__device__ __forceinline__ int sw_chunk(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
 __device__ __forceinline__ f32x4_t mma16(const u32x4& a, const u32x4& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -88,12 +96,15 @@ __device__ __forceinline__ void split8(const f32x4_t& v0, const f32x4_t& v1, u32
   }
 }
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) f4v gf4v;
+
 }  // namespace
 
 __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
   using T = uint16_t;
   using E = Elem<T>;
-  __shared__ u32x4 smem[kOffEnd];
+  __shared__ u32x4 smem[kLdsChunks];
 
   // matrix of this workgroup
   int bi = 0, b = blockIdx.x;
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
   // fp32 S_0 is staged over it
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   lds_sync();
-  float* const lf0 = reinterpret_cast<float*>(smem + kOffPh);
+  float* const lf0 = reinterpret_cast<float*>(smem + kOffStage);
   unroll<2>([&](auto i) {
     unroll<16>([&](auto r) {
       constexpr int I = decltype(i)::value, R = decltype(r)::value;
@@ -193,26 +204,35 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
       constexpr int KB = decltype(kb)::value;
       u32x4 hi, lo;
       split8(D[2 * KB], D[2 * KB + 1], hi, lo);
-      const int c = (cs + l16) * kPitch + 4 * KB + lq;
+      const int c = sw_chunk(cs + l16, 4 * KB + lq);
       smem[off_hi + c] = hi;
       smem[off_lo + c] = lo;
     });
   };
   // D += A B: A the split matrix at (off_hi, off_lo), B this wave's strip
-  // of a symmetric matrix in registers; three products per block.
+  // of a symmetric matrix in registers; three products per block.  The 32
+  // (K-block, row-block) steps run as one sequence with the A fragments
+  // read one step ahead, so that each step's LDS reads are in flight under
+  // the previous step's products.
   auto prod = [&](int off_hi, int off_lo, const f32x4_t (&B)[8], f32x4_t (&D)[8]) {
-    unroll<4>([&](auto kb) {
-      constexpr int KB = decltype(kb)::value;
-      u32x4 bh, bl;
-      split8(B[2 * KB], B[2 * KB + 1], bh, bl);
-      unroll<8>([&](auto i) {
-        constexpr int I = decltype(i)::value;
-        const int c = (16 * I + l16) * kPitch + 4 * KB + lq;
-        const u32x4 ah = smem[off_hi + c], al = smem[off_lo + c];
-        D[I] = mma16(ah, bh, D[I]);
-        D[I] = mma16(ah, bl, D[I]);
-        D[I] = mma16(al, bh, D[I]);
-      });
+    auto a_at = [&](int kb, int i) { return sw_chunk(16 * i + l16, 4 * kb + lq); };
+    u32x4 ah = smem[off_hi + a_at(0, 0)], al = smem[off_lo + a_at(0, 0)];
+    u32x4 bh, bl;
+    unroll<32>([&](auto t) {
+      constexpr int T = decltype(t)::value, KB = T / 8, I = T % 8;
+      if constexpr (I == 0) split8(B[2 * KB], B[2 * KB + 1], bh, bl);
+      u32x4 nh, nl;
+      if constexpr (T + 1 < 32) {
+        nh = smem[off_hi + a_at((T + 1) / 8, (T + 1) % 8)];
+        nl = smem[off_lo + a_at((T + 1) / 8, (T + 1) % 8)];
+      }
+      D[I] = mma16(ah, bh, D[I]);
+      D[I] = mma16(ah, bl, D[I]);
+      D[I] = mma16(al, bh, D[I]);
+      if constexpr (T + 1 < 32) {
+        ah = nh;
+        al = nl;
+      }
     });
   };
   auto zero8 = [](f32x4_t (&D)[8]) {
@@ -299,109 +319,145 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
 
   const MatDesc md = g.desc[b];
   const bool ori = md.oriented != 0;
-  float* const lf = reinterpret_cast<float*>(smem + kOffSh);
+  float* const lf = reinterpret_cast<float*>(smem + kOffStage);
+  float* const W = md.param;
+  const int64_t ldw = ori ? g.m_true : g.n_true;
   float sq = 0.0f;
-  for (int s = 0; s < kNSTA - 1; ++s) dma_stage(kOffRingA, s, min(s, nk2 - 1));
-  for (int j = 0; j < ntj; ++j) {
-    zero8(D);
-    unroll<2>([&](auto u) {               // the tile's two ring slots
-      const int kt2 = 2 * j + decltype(u)::value, cur = kt2 % kNSTA;
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNSTA - 2) * kSub));  // as in the X_0 X_0^T loop
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      barrier();
-      dma_stage(kOffRingA, cur == 0 ? kNSTA - 1 : cur - 1, min(kt2 + kNSTA - 1, nk2 - 1));
-      unroll<kSub>([&](auto h) {
-        constexpr int S = 2 * decltype(u)::value + decltype(h)::value;   // stage within the tile
-        const int base = kOffRingA + cur * kSlot + decltype(h)::value * kStage;
-        unroll<2>([&](auto ii) {
-          constexpr int I = 2 * S + decltype(ii)::value;                 // output block
-          unroll<4>([&](auto kb) {
-            const u32x4 a = frag_tr(base, decltype(kb)::value, decltype(ii)::value);
-            D[I] = mma16(a, qh[decltype(kb)::value], D[I]);
-            D[I] = mma16(a, ql[decltype(kb)::value], D[I]);
+  constexpr int kG = kT * kT / 4 / kNT;   // 16-byte W groups per thread and tile
+  // Group u of this thread in a full W tile: row rr, columns c4 .. c4 + 3 of
+  // the tile in W's orientation.  A global (not generic) pointer, so that
+  // the compiler's waits for these accesses count vector-memory operations
+  // only and do not drain the ring's loads in flight.
+  auto w_at = [&](int j, int u) -> gf4v* {
+    const int gidx = tid + u * kNT, rr = gidx >> 5, c4 = (gidx & 31) * 4;
+    const int64_t row0 = ori ? static_cast<int64_t>(j) * kT : 0;
+    const int64_t col0 = ori ? 0 : static_cast<int64_t>(j) * kT;
+    return (gf4v*)(W + (row0 + rr) * ldw + col0 + c4);
+  };
+  // Every tile is a full 128 x 128 block of W (m = 128 and n a multiple of
+  // 128): each tile's W loads are issued right after the tile's last ring
+  // slot, so that they are in flight under the tile's second half of
+  // products and the staging, and no load the compiler does not track
+  // follows them (its waits for W then hold back nothing else).  Loads
+  // complete in order, so a ring wait counts the loads issued after its
+  // slot: at least 12 from the second tile on (two slots and one tile's W
+  // loads), 4 (two slots) in the first.  Otherwise W is read after the
+  // staging, as a batch for full tiles or element by element for ragged
+  // ones, and the ring waits as in the X_0 X_0^T loop.
+  auto tile_loop = [&](auto full_c) {
+    constexpr bool kFull = decltype(full_c)::value;
+    for (int s = 0; s < kNSTA - 1; ++s) dma_stage(kOffRingA, s, min(s, nk2 - 1));
+    for (int j = 0; j < ntj; ++j) {
+      f4v w[kG];
+      zero8(D);
+      unroll<2>([&](auto u) {             // the tile's two ring slots
+        const int kt2 = 2 * j + decltype(u)::value, cur = kt2 % kNSTA;
+        if (kFull && j > 0) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kSub + kG));
+        } else {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm((kNSTA - 2) * kSub));
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        barrier();
+        dma_stage(kOffRingA, cur == 0 ? kNSTA - 1 : cur - 1, min(kt2 + kNSTA - 1, nk2 - 1));
+        if constexpr (kFull && decltype(u)::value == 1) {
+          // W is read and written once per step: non-temporal
+          unroll<kG>([&](auto v) {
+            w[decltype(v)::value] = __builtin_nontemporal_load(w_at(j, decltype(v)::value));
+          });
+        }
+        unroll<kSub>([&](auto h) {
+          constexpr int S = 2 * decltype(u)::value + decltype(h)::value;   // stage within the tile
+          const int base = kOffRingA + cur * kSlot + decltype(h)::value * kStage;
+          unroll<2>([&](auto ii) {
+            constexpr int I = 2 * S + decltype(ii)::value;                 // output block
+            unroll<4>([&](auto kb) {
+              const u32x4 a = frag_tr(base, decltype(kb)::value, decltype(ii)::value);
+              D[I] = mma16(a, qh[decltype(kb)::value], D[I]);
+              D[I] = mma16(a, ql[decltype(kb)::value], D[I]);
+            });
           });
         });
       });
-    });
 
-    // x = r D^T: lane (l16, lq) holds x[cs + l16][16 i + 4 lq + e] of the
-    // tile, staged in W's orientation; then W <- W - (lr wd W + step x),
-    // four consecutive W elements per group
-    unroll<8>([&](auto i) {
-      constexpr int I = decltype(i)::value;
-      const int rr = cs + l16, cc = 16 * I + 4 * lq;
-      const float v0 = r0 * D[I][0], v1 = r0 * D[I][1], v2 = r0 * D[I][2], v3 = r0 * D[I][3];
-      if (ori) {
-        lf[(cc + 0) * kApLd + rr] = v0;
-        lf[(cc + 1) * kApLd + rr] = v1;
-        lf[(cc + 2) * kApLd + rr] = v2;
-        lf[(cc + 3) * kApLd + rr] = v3;
+      // x = r D^T: lane (l16, lq) holds x[cs + l16][16 i + 4 lq + e] of the
+      // tile, staged in W's orientation; then W <- W - (lr wd W + step x),
+      // four consecutive W elements per group
+      unroll<8>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        const int rr = cs + l16, cc = 16 * I + 4 * lq;
+        const float v0 = r0 * D[I][0], v1 = r0 * D[I][1], v2 = r0 * D[I][2], v3 = r0 * D[I][3];
+        if (ori) {
+          lf[(cc + 0) * kApLd + rr] = v0;
+          lf[(cc + 1) * kApLd + rr] = v1;
+          lf[(cc + 2) * kApLd + rr] = v2;
+          lf[(cc + 3) * kApLd + rr] = v3;
+        } else {
+          *reinterpret_cast<float4*>(lf + rr * kApLd + cc) = make_float4(v0, v1, v2, v3);
+        }
+      });
+      lds_sync();
+      // W rows of this tile: X rows (plain) or X columns (oriented)
+      const int wrows = ori ? min(kT, g.n_true - j * kT) : g.m_true;
+      const int wcols = ori ? g.m_true : min(kT, g.n_true - j * kT);
+      const bool full = kFull || (wrows == kT && wcols == kT && (ldw % 4) == 0);
+      if (full) {
+        if constexpr (!kFull) {
+          // all of this thread's groups are loaded before any is updated
+          unroll<kG>([&](auto u) {
+            w[decltype(u)::value] = __builtin_nontemporal_load(w_at(j, decltype(u)::value));
+          });
+        }
+        unroll<kG>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          const int gidx = tid + U * kNT, rr = gidx >> 5, c4 = (gidx & 31) * 4;
+          const float4 x = *reinterpret_cast<const float4*>(lf + rr * kApLd + c4);
+          w[U][0] -= p.lrwd * w[U][0] + g.step * x.x;
+          w[U][1] -= p.lrwd * w[U][1] + g.step * x.y;
+          w[U][2] -= p.lrwd * w[U][2] + g.step * x.z;
+          w[U][3] -= p.lrwd * w[U][3] + g.step * x.w;
+          __builtin_nontemporal_store(w[U], w_at(j, U));
+          sq += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
+        });
       } else {
-        *reinterpret_cast<float4*>(lf + rr * kApLd + cc) = make_float4(v0, v1, v2, v3);
-      }
-    });
-    lds_sync();
-    // W rows of this tile: X rows (plain) or X columns (oriented)
-    const int64_t ldw = ori ? g.m_true : g.n_true;
-    const int wrows = ori ? min(kT, g.n_true - j * kT) : g.m_true;
-    const int wcols = ori ? g.m_true : min(kT, g.n_true - j * kT);
-    const int64_t row0 = ori ? static_cast<int64_t>(j) * kT : 0;
-    const int64_t col0 = ori ? 0 : static_cast<int64_t>(j) * kT;
-    float* const W = md.param;
-    const bool full = wrows == kT && wcols == kT && (ldw % 4) == 0;
-    if (full) {
-      // W is read and written once per step: non-temporal; all of this
-      // thread's groups are loaded before any is updated
-      typedef float f4v __attribute__((ext_vector_type(4)));
-      constexpr int kG = kT * kT / 4 / kNT;
-      f4v w[kG];
-      unroll<kG>([&](auto u) {
-        const int gidx = tid + decltype(u)::value * kNT, rr = gidx >> 5, c4 = (gidx & 31) * 4;
-        w[decltype(u)::value] =
-            __builtin_nontemporal_load(reinterpret_cast<const f4v*>(W + (row0 + rr) * ldw + col0 + c4));
-      });
-      unroll<kG>([&](auto u) {
-        constexpr int U = decltype(u)::value;
-        const int gidx = tid + U * kNT, rr = gidx >> 5, c4 = (gidx & 31) * 4;
-        const float4 x = *reinterpret_cast<const float4*>(lf + rr * kApLd + c4);
-        w[U][0] -= p.lrwd * w[U][0] + g.step * x.x;
-        w[U][1] -= p.lrwd * w[U][1] + g.step * x.y;
-        w[U][2] -= p.lrwd * w[U][2] + g.step * x.z;
-        w[U][3] -= p.lrwd * w[U][3] + g.step * x.w;
-        __builtin_nontemporal_store(w[U], reinterpret_cast<f4v*>(W + (row0 + rr) * ldw + col0 + c4));
-        sq += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
-      });
-    } else {
-      for (int gidx = tid; gidx < kT * kT / 4; gidx += kNT) {
-        const int rr = gidx >> 5, c4 = (gidx & 31) * 4;
-        if (rr >= wrows || c4 >= wcols) continue;
-        const float* xv = lf + rr * kApLd + c4;
-        float* wp = W + (row0 + rr) * ldw + col0 + c4;
-        for (int e = 0; e < 4 && c4 + e < wcols; ++e) {
-          const float x = xv[e];
-          wp[e] -= p.lrwd * wp[e] + g.step * x;
-          sq += x * x;
+        const int64_t row0 = ori ? static_cast<int64_t>(j) * kT : 0;
+        const int64_t col0 = ori ? 0 : static_cast<int64_t>(j) * kT;
+        for (int gidx = tid; gidx < kT * kT / 4; gidx += kNT) {
+          const int rr = gidx >> 5, c4 = (gidx & 31) * 4;
+          if (rr >= wrows || c4 >= wcols) continue;
+          const float* xv = lf + rr * kApLd + c4;
+          float* wp = W + (row0 + rr) * ldw + col0 + c4;
+          for (int e = 0; e < 4 && c4 + e < wcols; ++e) {
+            const float x = xv[e];
+            wp[e] -= p.lrwd * wp[e] + g.step * x;
+            sq += x * x;
+          }
         }
       }
-    }
-    if (g.rms_part) {
-      // per-tile partial (deterministic: fixed lanes and fixed order)
-      float t = sq;
+      if (g.rms_part) {
+        // per-tile partial (deterministic: fixed lanes and fixed order)
+        float t = sq;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-      lds_sync();                                     // staging reads done
-      float* red = reinterpret_cast<float*>(smem + kOffSh);
-      if (lane == 0) red[wave] = t;
-      lds_sync();
-      if (tid == 0) {
-        float tot = 0.0f;
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+        lds_sync();                                   // staging reads done
+        float* red = lf;                              // the ring is still in use
+        if (lane == 0) red[wave] = t;
+        lds_sync();
+        if (tid == 0) {
+          float tot = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) tot += red[w];
-        g.rms_part[static_cast<int64_t>(b) * ntj + j] = tot;
+          for (int w8 = 0; w8 < 8; ++w8) tot += red[w8];
+          g.rms_part[static_cast<int64_t>(b) * ntj + j] = tot;
+        }
+        sq = 0.0f;
       }
-      sq = 0.0f;
+      lds_sync();                                     // staging free for the next tile
     }
-    lds_sync();                                       // staging free for the next tile
+  };
+  if (g.m_true == kT && g.n_true % kT == 0) {
+    tile_loop(std::true_type{});
+  } else {
+    tile_loop(std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }

@@ -322,13 +322,14 @@ def test_small_matrix_fused_path(mod, ns_steps, scaling):
     """Shape groups of >= 32 matrices with m <= 128 take the fused kernel
     (the iteration carried out on m x m matrices at about fp32 precision,
     then X_N = Q X_0 and the apply, one workgroup per matrix): ragged and
-    oriented shapes, sampled matrices against the oracle, update RMS of
-    every matrix.  Its error is the bf16 storage of X_0, as in the CPU model
+    oriented shapes (m = 128 with n a multiple of 128 in both orientations
+    takes the kernel's full-tile W path), sampled matrices against the
+    oracle, update RMS of every matrix.  Its error is the bf16 storage of X_0, as in the CPU model
     ``bf16_model.ns_gram_space`` (test_bf16_model.py): off the square shape
     the bounds are that model's figures with a margin (1.6-2.1e-3 Frobenius
     measured at N <= 5), well inside the bf16 bar and at N = 10 below what
     bf16 iterates reach."""
-    groups = [((128, 512), 32), ((700, 96), 33), ((100, 300), 34), ((128, 128), 32)]
+    groups = [((128, 512), 32), ((700, 96), 33), ((100, 300), 34), ((128, 128), 32), ((384, 128), 32)]
     shapes = [s for s, n in groups for _ in range(n)]
     Ps, Gs, Ms = _mixed_state(1300 + ns_steps, shapes)
     P0 = [f64(p) for p in Ps]
