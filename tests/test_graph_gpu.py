@@ -32,10 +32,11 @@ def _state(seed, shapes, scale=1.0):
 
 @pytest.mark.parametrize("scaling", ["shape", "update_norm"])
 def test_plan_step_graph_replay(mod, scaling):
-    # the 33 [96, 300] matrices take the fused small-matrix kernel with the
-    # shape scaling (the update-norm scaling runs them through the general
-    # kernels)
-    shapes = [(300, 700), (700, 300), (512, 512), (1, 300)] + [(96, 300)] * 33
+    # the 33 [96, 300] matrices (ragged W tiles) and the 32 [128, 256]
+    # matrices (full W tiles, loaded ahead of the apply) take the fused
+    # small-matrix kernel with the shape scaling (the update-norm scaling
+    # runs them through the general kernels)
+    shapes = [(300, 700), (700, 300), (512, 512), (1, 300)] + [(96, 300)] * 33 + [(128, 256)] * 32
     Pe, Ge, Me = _state(5, shapes)
     Pg, Gg, Mg = [t.clone() for t in Pe], [t.clone() for t in Ge], [t.clone() for t in Me]
     pe = mod.MuonPlan(Pe, Ge, Me)
