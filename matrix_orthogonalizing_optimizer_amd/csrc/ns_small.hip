@@ -209,18 +209,48 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
       smem[off_lo + c] = lo;
     });
   };
+  // A strip kept split in registers (H[kb], L[kb]: the eight values of
+  // K-block kb), and stored from there.
+  auto split_strip = [](const f32x4_t (&D)[8], u32x4 (&H)[4], u32x4 (&L)[4]) {
+    unroll<4>([&](auto kb) {
+      constexpr int KB = decltype(kb)::value;
+      split8(D[2 * KB], D[2 * KB + 1], H[KB], L[KB]);
+    });
+  };
+  auto store_hl = [&](int off_hi, int off_lo, const u32x4 (&H)[4], const u32x4 (&L)[4]) {
+    unroll<4>([&](auto kb) {
+      constexpr int KB = decltype(kb)::value;
+      const int c = sw_chunk(cs + l16, 4 * KB + lq);
+      smem[off_hi + c] = H[KB];
+      smem[off_lo + c] = L[KB];
+    });
+  };
+  // B operand sources of the products: an fp32 strip split K-block by
+  // K-block as it is consumed, or a strip kept split.
+  auto b_f32 = [](const f32x4_t (&B)[8]) {
+    return [&B](auto kb, u32x4& h, u32x4& l) {
+      constexpr int KB = decltype(kb)::value;
+      split8(B[2 * KB], B[2 * KB + 1], h, l);
+    };
+  };
+  auto b_split = [](const u32x4 (&H)[4], const u32x4 (&L)[4]) {
+    return [&H, &L](auto kb, u32x4& h, u32x4& l) {
+      h = H[decltype(kb)::value];
+      l = L[decltype(kb)::value];
+    };
+  };
   // D += A B: A the split matrix at (off_hi, off_lo), B this wave's strip
   // of a symmetric matrix in registers; three products per block.  The 32
   // (K-block, row-block) steps run as one sequence with the A fragments
   // read one step ahead, so that each step's LDS reads are in flight under
   // the previous step's products.
-  auto prod = [&](int off_hi, int off_lo, const f32x4_t (&B)[8], f32x4_t (&D)[8]) {
+  auto prod = [&](int off_hi, int off_lo, auto&& b_of, f32x4_t (&D)[8]) {
     auto a_at = [&](int kb, int i) { return sw_chunk(16 * i + l16, 4 * kb + lq); };
     u32x4 ah = smem[off_hi + a_at(0, 0)], al = smem[off_lo + a_at(0, 0)];
     u32x4 bh, bl;
     unroll<32>([&](auto t) {
       constexpr int T = decltype(t)::value, KB = T / 8, I = T % 8;
-      if constexpr (I == 0) split8(B[2 * KB], B[2 * KB + 1], bh, bl);
+      if constexpr (I == 0) b_of(std::integral_constant<int, KB>{}, bh, bl);
       u32x4 nh, nl;
       if constexpr (T + 1 < 32) {
         nh = smem[off_hi + a_at((T + 1) / 8, (T + 1) % 8)];
@@ -240,8 +270,11 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
   };
 
   // this wave's strip of S_0 (its rows cs.. of the staged copy, S_0 being
-  // symmetric), then S_0 split into LDS
-  f32x4_t Ss[8], Ps[8], Qs[8], D[8];
+  // symmetric), then S_0 split into LDS.  P and Q are kept split in
+  // registers: P is split once for its store and the B operand of S P, Q
+  // once per step for the next P Q and, at the end, X_N.
+  f32x4_t Ss[8], D[8];
+  u32x4 ph[4], pl[4], qh[4], ql[4];
   unroll<8>([&](auto i) {
     constexpr int I = decltype(i)::value;
     const float4 v = *reinterpret_cast<const float4*>(lf0 + (cs + l16) * kApLd + 16 * I + 4 * lq);
@@ -254,48 +287,50 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
     const bool last = k + 1 == p.ns_steps;
     // P_k = a I + b S + c S S
     zero8(D);
-    prod(kOffSh, kOffSl, Ss, D);
-    unroll<8>([&](auto i) {
-      constexpr int I = decltype(i)::value;
-      unroll<4>([&](auto e) {
-        constexpr int Ei = decltype(e)::value;
-        float v = p.c * D[I][Ei] + p.b * Ss[I][Ei];
-        if (16 * I + 4 * lq + Ei == cs + l16) v += p.a;
-        Ps[I][Ei] = v;
+    prod(kOffSh, kOffSl, b_f32(Ss), D);
+    {
+      f32x4_t Ps[8];
+      unroll<8>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        unroll<4>([&](auto e) {
+          constexpr int Ei = decltype(e)::value;
+          float v = p.c * D[I][Ei] + p.b * Ss[I][Ei];
+          if (16 * I + 4 * lq + Ei == cs + l16) v += p.a;
+          Ps[I][Ei] = v;
+        });
       });
-    });
-    store_split(kOffPh, kOffPl, Ps);
+      split_strip(Ps, ph, pl);
+    }
+    store_hl(kOffPh, kOffPl, ph, pl);
     lds_sync();
+    // Q_{k+1} = P_k Q_k (P from LDS)
+    if (k == 0) {
+      unroll<4>([&](auto kb) {
+        qh[decltype(kb)::value] = ph[decltype(kb)::value];
+        ql[decltype(kb)::value] = pl[decltype(kb)::value];
+      });
+    } else {
+      zero8(D);
+      prod(kOffPh, kOffPl, b_split(qh, ql), D);
+      split_strip(D, qh, ql);
+    }
     if (!last) {
       // S_{k+1} = P (S P): T = S P first; every wave has read S before
       // S_{k+1} replaces it
       zero8(D);
-      prod(kOffSh, kOffSl, Ps, D);
+      prod(kOffSh, kOffSl, b_split(ph, pl), D);
       lds_sync();
       zero8(Ss);
-      prod(kOffPh, kOffPl, D, Ss);
+      prod(kOffPh, kOffPl, b_f32(D), Ss);
       store_split(kOffSh, kOffSl, Ss);
-    }
-    // Q_{k+1} = P_k Q_k
-    if (k == 0) {
-      unroll<8>([&](auto i) { Qs[decltype(i)::value] = Ps[decltype(i)::value]; });
-    } else {
-      zero8(D);
-      prod(kOffPh, kOffPl, Qs, D);
-      unroll<8>([&](auto i) { Qs[decltype(i)::value] = D[decltype(i)::value]; });
     }
     lds_sync();                           // P read by all; S_{k+1} visible
   }
 
   // -------- X_N = r Q X_0, 128 columns at a time, as (X_0^T Q)^T: for a
   // column tile j, D[n][c] = sum_k X_0[k][128 j + n] Q[k][c], with this
-  // wave's columns c = cs.. of Q (B, split once) and X_0^T (A) read from
+  // wave's columns c = cs.. of Q (B, kept split) and X_0^T (A) read from
   // the streamed stages with transposing LDS reads.
-  u32x4 qh[4], ql[4];
-  unroll<4>([&](auto kb) {
-    constexpr int KB = decltype(kb)::value;
-    split8(Qs[2 * KB], Qs[2 * KB + 1], qh[KB], ql[KB]);
-  });
   // A fragment: X_0 rows 32 kb + 4 lq + 0..3 and 32 kb + 16 + 4 lq + 0..3
   // of column 16 ii + l16 of a [128 rows][32] stage at chunk `base`.
   // Within each 16-lane group lane i points at row k0 + i / 4, columns
