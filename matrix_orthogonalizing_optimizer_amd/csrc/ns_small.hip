@@ -242,26 +242,29 @@ __global__ __launch_bounds__(512) void ns_small_kernel(SmallArgs p) {
   // D += A B: A the split matrix at (off_hi, off_lo), B this wave's strip
   // of a symmetric matrix in registers; three products per block.  The 32
   // (K-block, row-block) steps run as one sequence with the A fragments
-  // read one step ahead, so that each step's LDS reads are in flight under
-  // the previous step's products.
+  // read two steps ahead, so that each step's LDS reads are in flight under
+  // the two previous steps' products.
   auto prod = [&](int off_hi, int off_lo, auto&& b_of, f32x4_t (&D)[8]) {
     auto a_at = [&](int kb, int i) { return sw_chunk(16 * i + l16, 4 * kb + lq); };
     u32x4 ah = smem[off_hi + a_at(0, 0)], al = smem[off_lo + a_at(0, 0)];
+    u32x4 ah1 = smem[off_hi + a_at(0, 1)], al1 = smem[off_lo + a_at(0, 1)];
     u32x4 bh, bl;
     unroll<32>([&](auto t) {
       constexpr int T = decltype(t)::value, KB = T / 8, I = T % 8;
       if constexpr (I == 0) b_of(std::integral_constant<int, KB>{}, bh, bl);
       u32x4 nh, nl;
-      if constexpr (T + 1 < 32) {
-        nh = smem[off_hi + a_at((T + 1) / 8, (T + 1) % 8)];
-        nl = smem[off_lo + a_at((T + 1) / 8, (T + 1) % 8)];
+      if constexpr (T + 2 < 32) {
+        nh = smem[off_hi + a_at((T + 2) / 8, (T + 2) % 8)];
+        nl = smem[off_lo + a_at((T + 2) / 8, (T + 2) % 8)];
       }
       D[I] = mma16(ah, bh, D[I]);
       D[I] = mma16(ah, bl, D[I]);
       D[I] = mma16(al, bh, D[I]);
-      if constexpr (T + 1 < 32) {
-        ah = nh;
-        al = nl;
+      ah = ah1;
+      al = al1;
+      if constexpr (T + 2 < 32) {
+        ah1 = nh;
+        al1 = nl;
       }
     });
   };
