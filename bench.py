@@ -282,7 +282,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(every box here has a single MI355X)", file=sys.stderr)
+              "(the step runs whole matrices on one GPU, with no sharding or collectives)", file=sys.stderr)
         sys.exit(2)
     import torch
 

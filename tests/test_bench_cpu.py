@@ -3,7 +3,7 @@
 * The workloads reproduce the configurations' sizes: matrix counts, Muon
   and AdamW element counts, and the algorithmic Newton-Schulz flops per step
   (3 m^2 n + m^3 per matrix and iteration, m = min side).
-* ``bench.py --gpus N`` with N > 1 exits with a message (one GPU per box).
+* ``bench.py --gpus N`` with N > 1 exits with a message (the step runs on one GPU).
 * The calibrated-traffic lookup returns bytes only while the sha256 of the
   kernel sources it lists matches the tree, and None once they change.
 """
